@@ -1,0 +1,291 @@
+/*
+ * CPU oracle for paged MQA-logits scoring and per-row top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * statement of what the GPU path computes.  Only the test-suite, the smoke
+ * check and the benchmark's CPU-baseline leg load it; the product path never
+ * does.  It shares no source, header or helper with the HIP library.
+ *
+ * Arithmetic is float64 (inputs are bf16 / fp8 / f32, all exact in float64),
+ * loops run in the order the definition is written, and the file is compiled
+ * with -O2 -ffp-contract=off and without -ffast-math.  OpenMP only splits rows
+ * across threads; each output is computed by one thread in a fixed order.
+ *
+ * Sources (pages on the subject):
+ *  - ROCm/ATOM PR #2651, "Changes": a row's heads are scored against a key
+ *    column, ReLU is applied per head, then the heads are summed.
+ *  - sglang PR #48649, "Accuracy Tests": zero-padded heads add 0 after the ReLU.
+ *  - ROCm/aiter PR #4221, "Motivation" and "Technical details": fp8 e4m3 q and
+ *    keys, per-key f32 scale, f32 weights w[row, head], output f32; the
+ *    block-flat co-packed block (KVB key rows, then KVB f32 scales) and the
+ *    block-table gather kv_indices[b, col // KVB], slot col % KVB (commit
+ *    "extend fp8_paged_mqa_logits ... KVBlockSize>=1"); exact -inf mask gate.
+ *  - vLLM PR #62589, "Overview"/"Details": columns past a row's visible count
+ *    are masked; "Validation": top-k reads only [0, visible), compared as sets.
+ *
+ * Pins (tests/test_oracle_pins.py) tie every function here to something other
+ * than itself: library fp8/bf16 conversions, one-hot closed forms, GEMV special
+ * cases, invariants (zero heads, permutation, scale powers of two), and brute
+ * force over all subsets for the selection.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORA_OK 0
+#define ORA_E_ARG (-1)
+#define ORA_E_NAN (-2)
+#define ORA_E_TABLE (-3)
+
+/* bfloat16 is the top half of an IEEE binary32; widening is exact. */
+double ora_bf16_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * OCP 8-bit floating point, E4M3 "fn" variant (the fp8 e4m3 of ROCm/aiter
+ * PR #4221 on gfx950): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN;
+ * there are no infinities, so S.1111.110 = 448 is the largest magnitude.
+ */
+double ora_e4m3fn_to_double(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* fetch key column `col` of request `req` through the block table, dequantised
+ * to float64 (ROCm/aiter PR #4221 KVBlockSize commit; sglang PR #48649 test
+ * body: page_table rows index a [pages, page_size, 1, D] cache). */
+static int fetch_key(double *kd, int dtype, int layout, const void *kcache, const float *kscale,
+                     const int32_t *block_table, int max_blocks, int64_t num_blocks,
+                     int block_size, int head_dim, int req, int col)
+{
+    int32_t blk = block_table[(int64_t)req * max_blocks + col / block_size];
+    int slot = col % block_size;
+    if (blk < 0 || (int64_t)blk >= num_blocks)
+        return ORA_E_TABLE;
+    if (dtype == 0) {
+        const uint16_t *k = (const uint16_t *)kcache +
+                            ((int64_t)blk * block_size + slot) * head_dim;
+        for (int d = 0; d < head_dim; ++d)
+            kd[d] = ora_bf16_to_double(k[d]);
+        return ORA_OK;
+    }
+    const uint8_t *k;
+    double s = 1.0;
+    if (layout == 0) {
+        k = (const uint8_t *)kcache + ((int64_t)blk * block_size + slot) * head_dim;
+        if (kscale)
+            s = (double)kscale[(int64_t)blk * block_size + slot];
+    } else {
+        /* co-packed block: block_size key rows of head_dim bytes, then
+         * block_size little-endian f32 scales */
+        const uint8_t *base = (const uint8_t *)kcache +
+                              (int64_t)blk * block_size * (head_dim + 4);
+        float sf;
+        k = base + (int64_t)slot * head_dim;
+        memcpy(&sf, base + (int64_t)block_size * head_dim + 4 * slot, sizeof sf);
+        s = (double)sf;
+    }
+    /* dequantise, then dot: k_f[d] = fp8(k[d]) * scale */
+    for (int d = 0; d < head_dim; ++d)
+        kd[d] = ora_e4m3fn_to_double(k[d]) * s;
+    return ORA_OK;
+}
+
+/*
+ * logit[row, col] = sum_h w[row, h] * ReLU( sum_d q[row, h, d] * k[col, d] )
+ * for col < ctx_eff[row]; -inf for ctx_eff[row] <= col < width.
+ * ctx_eff = clamp(ctx[row], 0, min(width, max_blocks * block_size)).
+ * w == NULL means every weight is 1.
+ *
+ * `rows` selects which rows to compute (NULL: all); out is [n_rows][width].
+ */
+int ora_paged_logits(const void *q, int dtype, const float *w, const void *kcache, int layout,
+                     const float *kscale, const int32_t *block_table, const int32_t *ctx_lens,
+                     const int32_t *row_to_req, int num_rows, int num_heads, int head_dim,
+                     int block_size, int num_reqs, int max_blocks, int64_t num_blocks,
+                     int width, const int32_t *rows, int n_rows, double *out, int n_threads)
+{
+    if (!q || !kcache || !block_table || !ctx_lens || !row_to_req || !out)
+        return ORA_E_ARG;
+    if (num_rows < 0 || num_heads < 1 || head_dim < 1 || block_size < 1 || num_reqs < 1 ||
+        max_blocks < 1 || num_blocks < 1 || width < 0 || n_rows < 0)
+        return ORA_E_ARG;
+    if (dtype != 0 && dtype != 1)
+        return ORA_E_ARG;
+    if (dtype == 0 && layout != 0)
+        return ORA_E_ARG;
+    if (!rows)
+        n_rows = num_rows;
+    int64_t cap = (int64_t)max_blocks * block_size;
+    if (cap > width)
+        cap = width;
+    int status = ORA_OK;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int i = 0; i < n_rows; ++i) {
+        int row = rows ? rows[i] : i;
+        double *o = out + (int64_t)i * width;
+        if (row < 0 || row >= num_rows) {
+            status = ORA_E_ARG;
+            continue;
+        }
+        int req = row_to_req[row];
+        if (req < 0 || req >= num_reqs) {
+            status = ORA_E_ARG;
+            continue;
+        }
+        int64_t ctx = ctx_lens[row];
+        if (ctx < 0)
+            ctx = 0;
+        if (ctx > cap)
+            ctx = cap;
+        double *qd = (double *)malloc(sizeof(double) * (size_t)num_heads * head_dim);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)head_dim);
+        if (!qd || !kd) {
+            free(qd);
+            free(kd);
+            status = ORA_E_ARG;
+            continue;
+        }
+        for (int h = 0; h < num_heads; ++h)
+            for (int d = 0; d < head_dim; ++d) {
+                int64_t at = ((int64_t)row * num_heads + h) * head_dim + d;
+                qd[h * head_dim + d] = dtype == 0
+                                           ? ora_bf16_to_double(((const uint16_t *)q)[at])
+                                           : ora_e4m3fn_to_double(((const uint8_t *)q)[at]);
+            }
+        for (int64_t col = 0; col < ctx; ++col) {
+            if (fetch_key(kd, dtype, layout, kcache, kscale, block_table, max_blocks, num_blocks,
+                          block_size, head_dim, req, (int)col) != ORA_OK) {
+                status = ORA_E_TABLE;
+                o[col] = NAN;
+                continue;
+            }
+            double acc = 0.0;
+            for (int h = 0; h < num_heads; ++h) {
+                double dot = 0.0;
+                for (int d = 0; d < head_dim; ++d)
+                    dot += qd[h * head_dim + d] * kd[d];
+                double relu = dot > 0.0 ? dot : 0.0;
+                double wh = w ? (double)w[(int64_t)row * num_heads + h] : 1.0;
+                acc += wh * relu;
+            }
+            o[col] = acc;
+        }
+        for (int64_t col = ctx; col < width; ++col)
+            o[col] = -INFINITY;
+        free(qd);
+        free(kd);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* per-row top-k                                                              */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    float v;
+    int32_t i;
+} ora_cand;
+
+/* larger value first; equal values (+0 and -0 are equal) by lower column */
+static int cand_cmp(const void *pa, const void *pb)
+{
+    const ora_cand *a = (const ora_cand *)pa, *b = (const ora_cand *)pb;
+    if (a->v > b->v)
+        return -1;
+    if (a->v < b->v)
+        return 1;
+    return (a->i > b->i) - (a->i < b->i);
+}
+
+/*
+ * Per row: the min(k, n) columns of [0, n), n = clamp(ctx[row], 0, width),
+ * with the largest logits; among equal logits the lower column is kept.
+ * Slots past min(k, n) hold -1.  Emitted in (value desc, column asc) order;
+ * the contract is the set (vLLM PR #62589, Validation: compared as sets;
+ * sglang PR #48649 test body: entries < 0 are padding).
+ * Returns ORA_E_NAN when a NaN lies inside [0, n): a precondition violation.
+ */
+int ora_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int num_rows,
+             int width, int k, int32_t *idx_out, int n_threads)
+{
+    if (!logits || !ctx_lens || !idx_out || num_rows < 0 || width < 0 || k < 1 ||
+        stride < width)
+        return ORA_E_ARG;
+    int status = ORA_OK;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int row = 0; row < num_rows; ++row) {
+        int64_t n = ctx_lens[row];
+        if (n < 0)
+            n = 0;
+        if (n > width)
+            n = width;
+        int32_t *o = idx_out + (int64_t)row * k;
+        ora_cand *c = (ora_cand *)malloc(sizeof(ora_cand) * (size_t)(n > 0 ? n : 1));
+        if (!c) {
+            status = ORA_E_ARG;
+            continue;
+        }
+        const float *x = logits + (int64_t)row * stride;
+        int bad = 0;
+        for (int64_t j = 0; j < n; ++j) {
+            c[j].v = x[j];
+            c[j].i = (int32_t)j;
+            if (isnan(x[j]))
+                bad = 1;
+        }
+        if (bad) {
+            status = ORA_E_NAN;
+            for (int j = 0; j < k; ++j)
+                o[j] = -1;
+            free(c);
+            continue;
+        }
+        qsort(c, (size_t)n, sizeof(ora_cand), cand_cmp);
+        int64_t take = n < k ? n : k;
+        for (int64_t j = 0; j < take; ++j)
+            o[j] = c[j].i;
+        for (int64_t j = take; j < k; ++j)
+            o[j] = -1;
+        free(c);
+    }
+    return status;
+}
+
+int ora_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
