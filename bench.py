@@ -1,0 +1,222 @@
+"""Benchmark: one paged MQA-logits + top-k call per step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_verify]
+
+Prints one JSON line.  The default workload is the decode-verify batch
+(9 requests x 4 MTP rows, 4 index heads, D = 128, bf16, contexts uniform in
+16,000..32,000 compressed columns, block 16, top-k 2048).  Inputs are seeded and
+synthetic and already resident in HBM when timing starts; the step cycles
+through enough input replicas that no step finds its keys in L2 or the 256 MB
+Infinity Cache (each replica's bytes are read again only after more than
+512 MB of other traffic).
+
+``value`` is microseconds per call (scoring + selection), timed with HIP events
+around the K steps.  ``roofline`` covers the scoring kernel: algorithmic bytes
+per launch / the mean duration of its launches (events recorded on the stream
+the kernels run on), against the MI355X HBM peak of 8 TB/s.  ``cpu_baseline`` is
+the CPU oracle timed on this host's cores on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per paged MQA-logits+top-k call; achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_logits_block_amd", "csrc", f)
+                  for f in ("logits.hip", "qsa_device.h", "qsa_internal.h")]
+
+DESCRIPTIONS = {
+    "tiny": "2 requests x 4 rows, 4 heads, D=128, bf16, ctx 1000/3000, block 16, top-k 256",
+    "decode_verify": "9 requests x 4 MTP rows (36 rows), 4 heads, D=128, bf16 q/k N(0,1), "
+                     "ctx U[16000,32000] compressed columns, block 16, top-k 2048",
+    "single_row_mixed": "64 requests x 1 row, 4 heads zero-padded to 16, D=128, bf16, "
+                        "ctx log-uniform 5000..65600, width 65600, block 64, top-k 2048",
+    "fp8_paged": "16 requests x 4 rows, 64 heads, D=128, fp8 e4m3 q/k, per-key f32 scale, "
+                 "w U(0,1), kv_len 32768, co-packed KVB=64, top-k 2048",
+    "prefill_chunk": "1 request, 16384 rows at positions 98304..114687, 4 heads, D=128, bf16, "
+                     "ctx (pos+1)//4, block 64, top-k 2048",
+}
+
+
+def algorithmic_bytes(inp):
+    """Bytes the scoring must move at least once: keys (and scales) once per
+    request, q, w, the table entries used, ctx / row_to_req, and every output
+    column (-inf included)."""
+    import numpy as np
+    B = inp.block_size
+    kv = np.zeros(inp.num_reqs, dtype=np.int64)
+    ce = inp.ctx_eff()
+    for r in range(inp.num_rows):
+        kv[inp.row_to_req[r]] = max(kv[inp.row_to_req[r]], int(ce[r]))
+    key_b = inp.key_bytes_per_col()
+    qb = inp.q.nbytes + (0 if inp.w is None else inp.w.nbytes)
+    table = int(np.sum((kv + B - 1) // B)) * 4
+    reads = int(np.sum(kv)) * key_b + qb + table + 8 * inp.num_rows
+    writes = inp.num_rows * inp.width * 4
+    return reads, writes
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    once the kernel sources differ from the ones the counters were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s=20.0):
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    # time one call on a row sample that keeps the run within the budget
+    rows = list(range(inp.num_rows))
+    t0 = time.perf_counter()
+    oracle.paged_logits(inp, rows=rows[:1])
+    one = max(time.perf_counter() - t0, 1e-4)
+    n = max(1, min(inp.num_rows, int(budget_s / 3 / one)))
+    n -= n % max(1, min(n, 4))
+    sample = rows[:max(n, 1)]
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        lg = oracle.paged_logits(inp, rows=sample)
+        oracle.topk(lg.astype(np.float32), inp.ctx_lens[sample], inp.topk)
+        times.append(time.perf_counter() - t0)
+    per_call_us = statistics.median(times) * 1e6 * inp.num_rows / len(sample)
+    return {"value": round(per_call_us, 1), "unit": "µs/call", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} of {inp.num_rows} rows, scoring + top-k, median of 3, "
+                      f"scaled by rows; float64 C loops, OpenMP over rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_verify", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the scoring path has no multi-GPU variant in this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_each_way": n * 4}))
+        return
+
+    import paged_mqa_logits_block_amd as qsa
+    import qsa_inputs
+    from qsa_inputs.device import to_device
+
+    inp = qsa_inputs.make_config(args.workload)
+    reads, writes = algorithmic_bytes(inp)
+    per_call = reads + writes
+    reps = max(1, min(16, math.ceil(600e6 / max(inp.kcache.nbytes + writes, 1))))
+    devs = [to_device(inp) for _ in range(reps)]
+    outs = [torch.empty((inp.num_rows, inp.width), dtype=torch.float32, device="cuda") for _ in range(reps)]
+    idx = torch.empty((inp.num_rows, inp.topk), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        d, o = devs[i % reps], outs[i % reps]
+        if evs is not None:
+            evs[0].record(stream)
+        qsa.paged_logits(d.q, d.kcache, d.block_table, d.ctx_lens, d.row_to_req, width=d.width,
+                         block_size=d.block_size, w=d.w, kscale=d.kscale, layout=d.layout, out=o,
+                         stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        qsa.topk(o, d.ctx_lens, d.topk, out=idx, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps; per-launch events on the stream the
+    # kernels run on give each kernel's mean duration
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    us_per_call = total_ms * 1e3 / args.steps
+    logit_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    topk_us = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+
+    achieved = per_call / (logit_us * 1e-6) / 1e9
+    traffic = measured_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(us_per_call, 2),
+        "unit": "µs/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic (seeded generators; shapes of the pages' workloads)",
+        "config": {"workload": args.workload, "description": DESCRIPTIONS[args.workload],
+                   "rows": inp.num_rows, "width": inp.width, "heads": inp.num_heads,
+                   "block": inp.block_size, "topk": inp.topk, "input_replicas": reps},
+        "logits_us": round(logit_us, 2),
+        "topk_us": round(topk_us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "paged_logits_kernel", "algorithmic_bytes": per_call,
+                     "algorithmic_read_bytes": reads, "algorithmic_write_bytes": writes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

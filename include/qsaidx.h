@@ -1,0 +1,169 @@
+/*
+ * qsaidx.h -- paged MQA-logits scoring and per-row top-k for a sparse-attention
+ * (QSA-style) indexer, on AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for every query row r with H index heads of dimension
+ * D, and every compressed key column c of the row's request:
+ *
+ *     logit[r, c] = sum_h w[r, h] * ReLU( q[r, h, :] . k[c, :] )      c <  ctx[r]
+ *     logit[r, c] = -inf                                             ctx[r] <= c < width
+ *
+ * The ReLU is applied per head, before the heads are summed (ROCm/ATOM PR #2651,
+ * "Changes"); zero-padded heads therefore add exactly 0 (sglang PR #48649,
+ * "Accuracy Tests").  w is an f32 weight per (row, head), or 1 when absent
+ * (ROCm/aiter PR #4221, "Motivation" and "Technical details").  For fp8 keys with
+ * a per-key f32 scale s[c], k[c, :] is the dequantised key fp8(k8[c, :]) * s[c]
+ * (same page).  Key column c of request b lives in pool block
+ * block_table[b, c / B] at slot c % B (same page, block-flat commit; sglang
+ * PR #48649 test body).  Columns past a row's visible count are -inf (ROCm/aiter
+ * PR #4221 test gate "exact -inf mask").
+ *
+ * qsa_topk then selects, per row, the k columns of [0, ctx[r]) with the largest
+ * logits (vLLM PR #62589, "Details": top-k reads only [0, visible); sglang
+ * PR #48649: rows that fit in k keep everything).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is DEVICE memory owned by the caller, unless stated.
+ *    The library allocates nothing, keeps no pointer after returning, and has no
+ *    global state other than a thread-local error message.
+ *  - Compute calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  They never synchronise the device or read device memory on the
+ *    host, so they may be captured into a HIP graph.
+ *  - Only host-visible scalars are validated; a failed validation returns a
+ *    status with no launch.  Device values are preconditions, listed per call.
+ *  - No call aborts or throws.  qsa_last_error() describes the last non-OK
+ *    status of the calling thread.
+ */
+#ifndef QSAIDX_H
+#define QSAIDX_H
+
+#include <stdint.h>
+
+#ifndef QSA_API
+#define QSA_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_E_INVALID = 1,     /* null pointer, negative or inconsistent size          */
+    QSA_E_DTYPE = 2,       /* unknown dtype, or q and k dtypes differ               */
+    QSA_E_UNSUPPORTED = 3, /* valid request outside the compiled set (see below)    */
+    QSA_E_RANGE = 4,       /* a size or offset exceeds what the kernels address     */
+    QSA_E_ALIGN = 5,       /* pointer or stride misaligned                          */
+    QSA_E_HIP = 6          /* the HIP runtime rejected the launch                  */
+} qsa_status;
+
+typedef enum qsa_dtype {
+    QSA_BF16 = 0,          /* bfloat16 q and keys                                   */
+    QSA_FP8_E4M3FN = 1     /* OCP fp8 E4M3 ("fn": no infinities, max 448) q and keys */
+} qsa_dtype;
+
+typedef enum qsa_kv_layout {
+    /* kcache is [num_blocks][block_size][head_dim] elements; for fp8 an optional
+     * separate kscale [num_blocks][block_size] f32.                             */
+    QSA_KV_PAGED = 0,
+    /* fp8 only, block-flat co-packed (ROCm/aiter PR #4221, block-flat commit):
+     * each block is block_size*head_dim key bytes (key of slot s at byte
+     * s*head_dim) followed by block_size little-endian f32 scales (slot s at
+     * byte block_size*head_dim + 4*s); block stride block_size*(head_dim+4).  */
+    QSA_KV_COPACKED = 1
+} qsa_kv_layout;
+
+typedef struct qsa_logits_shape {
+    int32_t num_rows;    /* R query rows                                           */
+    int32_t num_heads;   /* H index heads per row, zero-padded heads included      */
+    int32_t head_dim;    /* D                                                      */
+    int32_t block_size;  /* B key COLUMNS per pool block                           */
+    int32_t num_reqs;    /* rows of block_table                                    */
+    int32_t max_blocks;  /* columns of block_table                                 */
+    int32_t width;       /* W logits written per row                               */
+    int32_t q_dtype;     /* qsa_dtype                                              */
+    int32_t k_dtype;     /* qsa_dtype; must equal q_dtype                          */
+    int32_t kv_layout;   /* qsa_kv_layout                                          */
+    int64_t num_blocks;  /* blocks in the key pool                                 */
+    int64_t out_stride;  /* floats between consecutive rows of out, >= width       */
+} qsa_logits_shape;
+
+/*
+ * qsa_paged_logits -- the masked logits [R][W] (formula at the top of this file).
+ *
+ *   q           [R][H][D] elements of q_dtype, row-major; rows of one request may
+ *               sit anywhere, but request-major order lets rows share key reads.
+ *   w           [R][H] f32, or NULL for w = 1.
+ *   kcache      key pool in kv_layout (see qsa_kv_layout).
+ *   kscale      QSA_KV_PAGED + fp8: [num_blocks][B] f32 or NULL (scale 1).
+ *               Must be NULL for bf16 and for QSA_KV_COPACKED.
+ *   block_table [num_reqs][max_blocks] int32 pool block indices.
+ *   ctx_lens    [R] int32 visible columns per row.
+ *   row_to_req  [R] int32 row -> block_table row.
+ *   out         [R][out_stride] f32; columns [0, W) of every row are written,
+ *               columns [W, out_stride) are not touched.
+ *
+ * Visible count: ctx_eff[r] = clamp(ctx_lens[r], 0, min(W, max_blocks*B)).
+ * Device preconditions: 0 <= row_to_req[r] < num_reqs; the first
+ * ceil(ctx_eff/B) table entries of each row's request index blocks of the pool;
+ * fp8 scales are >= 0 (the scale is applied after the ReLU, which equals
+ * applying it to the key only for non-negative scales).  Out-of-range indices are
+ * never dereferenced: a row_to_req value outside [0, num_reqs) makes that row's
+ * visible columns NaN, and a table entry outside [0, num_blocks) makes the 16
+ * columns of every tile it would feed NaN.
+ *
+ * Compiled set (else QSA_E_UNSUPPORTED): D = 128; H in {1,2,4,8,16,32,64};
+ * B a multiple of 16 in [16, 1024]; bf16 + PAGED, fp8 + PAGED, fp8 + COPACKED.
+ * Alignment (else QSA_E_ALIGN): q, kcache, out 16-byte aligned; out_stride % 4 == 0.
+ * Range (else QSA_E_RANGE): W <= 1<<24; R*out_stride*4 and num_blocks*block
+ * bytes below 2^62.
+ */
+QSA_API qsa_status qsa_paged_logits(const void *q, const float *w, const void *kcache,
+                            const float *kscale, const int32_t *block_table,
+                            const int32_t *ctx_lens, const int32_t *row_to_req, float *out,
+                            const qsa_logits_shape *shape, void *stream);
+
+/* Validation of qsa_paged_logits' host-visible arguments only: no HIP call, no
+ * launch.  Returns what qsa_paged_logits would return before launching. */
+QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const void *kcache,
+                                  const float *kscale, const int32_t *block_table,
+                                  const int32_t *ctx_lens, const int32_t *row_to_req,
+                                  const float *out, const qsa_logits_shape *shape);
+
+/*
+ * qsa_topk -- per row r, the k columns of [0, n_r), n_r = clamp(ctx_lens[r], 0,
+ * width), with the largest logits; equal logits (+0 and -0 are equal) are broken
+ * toward the lower column.  Rows with n_r <= k keep all of [0, n_r).
+ *
+ *   logits   [num_rows][logits_stride] f32 (the buffer holds num_rows *
+ *            logits_stride floats); only columns [0, n_r) decide the result
+ *            (reads are rounded up to a multiple of 4 columns).
+ *   ctx_lens [num_rows] int32.
+ *   idx_out  [num_rows][k] int32: the selected columns in ascending order, then
+ *            -1 in slots [min(k, n_r), k).  The order is part of this
+ *            implementation, not of the selection's definition (a set).
+ *
+ * Device precondition: no NaN inside [0, n_r) (a NaN ranks by its bit pattern:
+ * above +inf when its sign is clear, below -inf when set).
+ * Compiled set (else QSA_E_UNSUPPORTED): 1 <= k <= 2048; width <= 69632.
+ * Alignment (else QSA_E_ALIGN): logits 16-byte aligned, logits_stride % 4 == 0.
+ */
+QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                    int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out, void *stream);
+
+/* Validation of qsa_topk's host-visible arguments only: no HIP call, no launch. */
+QSA_API qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                          int32_t num_rows, int32_t width, int32_t k, const int32_t *idx_out);
+
+/* Message for the calling thread's last non-OK status ("" if none). Owned by the
+ * library; valid until the thread's next call. */
+QSA_API const char *qsa_last_error(void);
+
+/* Library version string, e.g. "qsaidx 0.1.0 gfx950". */
+QSA_API const char *qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSAIDX_H */

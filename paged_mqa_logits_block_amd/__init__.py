@@ -1,0 +1,182 @@
+"""Python binding of libqsaidx: paged MQA-logits scoring and per-row top-k on
+MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/qsaidx.h``.  Tensors are torch
+device tensors (torch is used for device memory and streams); calls are queued
+on the current torch stream unless ``stream`` is given.  Importing this module
+fails loudly when the compiled library is absent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsaidx.so")
+
+# qsa_status
+OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_RANGE, E_ALIGN, E_HIP = range(7)
+STATUS_NAMES = {0: "QSA_OK", 1: "QSA_E_INVALID", 2: "QSA_E_DTYPE", 3: "QSA_E_UNSUPPORTED",
+                4: "QSA_E_RANGE", 5: "QSA_E_ALIGN", 6: "QSA_E_HIP"}
+# qsa_dtype / qsa_kv_layout
+BF16, FP8_E4M3FN = 0, 1
+KV_PAGED, KV_COPACKED = 0, 1
+
+EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_check", "qsa_topk", "qsa_topk_check",
+            "qsa_last_error", "qsa_version")
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class LogitsShape(ctypes.Structure):
+    _fields_ = [
+        ("num_rows", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_reqs", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("width", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+        ("k_dtype", ctypes.c_int32), ("kv_layout", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64), ("out_stride", ctypes.c_int64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32p, i64, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sp = ctypes.POINTER(LogitsShape)
+    lib.qsa_paged_logits.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp, vp]
+    lib.qsa_paged_logits.restype = ctypes.c_int
+    lib.qsa_paged_logits_check.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp]
+    lib.qsa_paged_logits_check.restype = ctypes.c_int
+    lib.qsa_topk.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp]
+    lib.qsa_topk.restype = ctypes.c_int
+    lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32, i32, i32, i32p]
+    lib.qsa_topk_check.restype = ctypes.c_int
+    lib.qsa_last_error.argtypes = []
+    lib.qsa_last_error.restype = ctypes.c_char_p
+    lib.qsa_version.argtypes = []
+    lib.qsa_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def version() -> str:
+    return lib.qsa_version().decode()
+
+
+def last_error() -> str:
+    return lib.qsa_last_error().decode()
+
+
+def _raise_on(status: int):
+    if status != OK:
+        raise QsaError(status, last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP8_E4M3FN
+    raise QsaError(E_DTYPE, f"unsupported tensor dtype {t.dtype}")
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise QsaError(E_INVALID, msg)
+
+
+def make_shape(q, kcache, block_table, *, width: int, block_size: int, layout: int = KV_PAGED,
+               out_stride: Optional[int] = None, num_blocks: Optional[int] = None) -> LogitsShape:
+    R, H, D = (int(x) for x in q.shape)
+    return LogitsShape(
+        num_rows=R, num_heads=H, head_dim=D, block_size=int(block_size),
+        num_reqs=int(block_table.shape[0]), max_blocks=int(block_table.shape[1]),
+        width=int(width), q_dtype=_dtype_code(q), k_dtype=_dtype_code(kcache),
+        kv_layout=int(layout),
+        num_blocks=int(kcache.shape[0] if num_blocks is None else num_blocks),
+        out_stride=int(width if out_stride is None else out_stride))
+
+
+def paged_logits(q, kcache, block_table, ctx_lens, row_to_req, *, width: int, block_size: int,
+                 w=None, kscale=None, layout: int = KV_PAGED, out=None, stream=None):
+    """``qsa_paged_logits``: f32 logits ``[R, width]`` (or into ``out``, whose row
+    stride may exceed ``width``).  See include/qsaidx.h for the contract."""
+    import torch
+    for name, t in (("q", q), ("kcache", kcache), ("block_table", block_table),
+                    ("ctx_lens", ctx_lens), ("row_to_req", row_to_req), ("w", w), ("kscale", kscale)):
+        if t is not None:
+            _require(t.is_cuda, f"{name} must be a device tensor")
+            _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(q.dim() == 3, "q must be [R, H, D]")
+    for name, t in (("block_table", block_table), ("ctx_lens", ctx_lens), ("row_to_req", row_to_req)):
+        _require(t.dtype == torch.int32, f"{name} must be int32")
+    if w is not None:
+        _require(w.dtype == torch.float32 and tuple(w.shape) == tuple(q.shape[:2]), "w must be f32 [R, H]")
+    if kscale is not None:
+        _require(kscale.dtype == torch.float32, "kscale must be f32")
+    R = int(q.shape[0])
+    _require(int(ctx_lens.numel()) == R and int(row_to_req.numel()) == R, "ctx_lens / row_to_req must have R entries")
+    if out is None:
+        out = torch.empty((R, width), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.dim() == 2 and out.stride(1) == 1, "out must be f32 [R, >=width]")
+    shape = make_shape(q, kcache, block_table, width=width, block_size=block_size, layout=layout,
+                       out_stride=out.stride(0) if R > 0 else width)
+    st = lib.qsa_paged_logits(_ptr(q), _ptr(w), _ptr(kcache), _ptr(kscale), _ptr(block_table),
+                              _ptr(ctx_lens), _ptr(row_to_req), _ptr(out), ctypes.byref(shape),
+                              _stream(stream))
+    _raise_on(st)
+    return out
+
+
+def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, stream=None):
+    """``qsa_topk``: int32 ``[R, k]`` selected columns, ascending, -1 padded."""
+    import torch
+    _require(logits.is_cuda and ctx_lens.is_cuda, "logits and ctx_lens must be device tensors")
+    _require(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
+             "logits must be f32 [R, >=width] with unit column stride")
+    _require(ctx_lens.dtype == torch.int32 and ctx_lens.is_contiguous(), "ctx_lens must be contiguous int32")
+    R = int(logits.shape[0])
+    width = int(logits.shape[1]) if width is None else int(width)
+    if out is None:
+        out = torch.empty((R, k), dtype=torch.int32, device=logits.device)
+    _require(out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (R, k),
+             "out must be contiguous int32 [R, k]")
+    stride = int(logits.stride(0)) if R > 0 else width
+    st = lib.qsa_topk(_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), _stream(stream))
+    _raise_on(st)
+    return out
+
+
+def paged_logits_check(q_ptr, w_ptr, kcache_ptr, kscale_ptr, bt_ptr, ctx_ptr, r2r_ptr, out_ptr,
+                       shape: LogitsShape) -> int:
+    """Host-side validation only (``qsa_paged_logits_check``); pointers are ints."""
+    return lib.qsa_paged_logits_check(q_ptr, w_ptr, kcache_ptr, kscale_ptr, bt_ptr, ctx_ptr, r2r_ptr,
+                                      out_ptr, ctypes.byref(shape))
+
+
+def topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr) -> int:
+    """Host-side validation only (``qsa_topk_check``); pointers are ints."""
+    return lib.qsa_topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr)

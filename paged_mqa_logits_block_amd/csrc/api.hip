@@ -1,0 +1,170 @@
+// C-ABI entry points of libqsaidx: argument validation, variant choice and
+// launches.  Validation reads host scalars only; nothing here synchronises the
+// device or reads device memory, so every call can be graph-captured
+// (vLLM PR #62589, Dispatch: host values only, no device sync).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qsa_internal.h"
+#include "qsaidx.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status fail(qsa_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qsa_status ok() {
+    g_err[0] = '\0';
+    return QSA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 62;
+
+qsa_status check_logits(const void *q, const float *w, const void *kcache, const float *kscale,
+                        const int32_t *block_table, const int32_t *ctx_lens,
+                        const int32_t *row_to_req, const float *out, const qsa_logits_shape *s) {
+    (void)w;
+    if (!s) return fail(QSA_E_INVALID, "shape is NULL");
+    if (s->num_rows < 0) return fail(QSA_E_INVALID, "num_rows = %d < 0", s->num_rows);
+    if (s->width < 0) return fail(QSA_E_INVALID, "width = %d < 0", s->width);
+    if (s->num_heads < 1 || s->head_dim < 1 || s->block_size < 1 || s->num_reqs < 1 ||
+        s->max_blocks < 1 || s->num_blocks < 1)
+        return fail(QSA_E_INVALID,
+                    "num_heads, head_dim, block_size, num_reqs, max_blocks and num_blocks must be >= 1");
+    if (s->out_stride < s->width)
+        return fail(QSA_E_INVALID, "out_stride = %lld < width = %d", (long long)s->out_stride, s->width);
+    const bool empty = s->num_rows == 0 || s->width == 0;
+    if (!empty && (!q || !kcache || !block_table || !ctx_lens || !row_to_req || !out))
+        return fail(QSA_E_INVALID, "q, kcache, block_table, ctx_lens, row_to_req and out must be non-NULL");
+    if ((s->q_dtype != QSA_BF16 && s->q_dtype != QSA_FP8_E4M3FN) ||
+        (s->k_dtype != QSA_BF16 && s->k_dtype != QSA_FP8_E4M3FN))
+        return fail(QSA_E_DTYPE, "unknown dtype (q %d, k %d)", s->q_dtype, s->k_dtype);
+    if (s->q_dtype != s->k_dtype)
+        return fail(QSA_E_DTYPE, "q and k dtypes differ (q %d, k %d)", s->q_dtype, s->k_dtype);
+    if (s->kv_layout != QSA_KV_PAGED && s->kv_layout != QSA_KV_COPACKED)
+        return fail(QSA_E_INVALID, "unknown kv_layout %d", s->kv_layout);
+    if (s->kv_layout == QSA_KV_COPACKED && s->k_dtype != QSA_FP8_E4M3FN)
+        return fail(QSA_E_UNSUPPORTED, "the co-packed layout holds fp8 keys only");
+    if (kscale && (s->k_dtype != QSA_FP8_E4M3FN || s->kv_layout != QSA_KV_PAGED))
+        return fail(QSA_E_INVALID, "kscale applies to fp8 keys in the paged layout only");
+    if (s->head_dim != 128) return fail(QSA_E_UNSUPPORTED, "head_dim = %d (only 128 is built)", s->head_dim);
+    const int H = s->num_heads;
+    if (H > 64 || (H & (H - 1)) != 0)
+        return fail(QSA_E_UNSUPPORTED, "num_heads = %d (built: 1, 2, 4, 8, 16, 32, 64)", H);
+    if (s->block_size % 16 != 0 || s->block_size > 1024)
+        return fail(QSA_E_UNSUPPORTED, "block_size = %d (built: multiples of 16 up to 1024)", s->block_size);
+    if (s->width > (1 << 24)) return fail(QSA_E_RANGE, "width = %d > 2^24", s->width);
+    if ((int64_t)s->num_rows * s->out_stride > kMaxBytes / 4)
+        return fail(QSA_E_RANGE, "num_rows * out_stride too large");
+    const int64_t elt = s->k_dtype == QSA_BF16 ? 2 : 1;
+    const int64_t block_bytes = (int64_t)s->block_size * s->head_dim * elt +
+                                (s->kv_layout == QSA_KV_COPACKED ? 4 * (int64_t)s->block_size : 0);
+    if (s->num_blocks > kMaxBytes / block_bytes) return fail(QSA_E_RANGE, "key pool too large");
+    if ((int64_t)s->num_reqs * s->max_blocks > ((int64_t)1 << 40))
+        return fail(QSA_E_RANGE, "block table too large");
+    if (!empty && (!aligned16(q) || !aligned16(kcache) || !aligned16(out)))
+        return fail(QSA_E_ALIGN, "q, kcache and out must be 16-byte aligned");
+    if (!empty && s->out_stride % 4 != 0) return fail(QSA_E_ALIGN, "out_stride must be a multiple of 4");
+    return ok();
+}
+
+qsa_status check_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int32_t num_rows,
+                      int32_t width, int32_t k, const int32_t *idx_out) {
+    if (num_rows < 0) return fail(QSA_E_INVALID, "num_rows = %d < 0", num_rows);
+    if (width < 0) return fail(QSA_E_INVALID, "width = %d < 0", width);
+    if (k < 1) return fail(QSA_E_INVALID, "k = %d < 1", k);
+    if (stride < width) return fail(QSA_E_INVALID, "logits_stride = %lld < width = %d", (long long)stride, width);
+    if (num_rows > 0 && (!logits || !ctx_lens || !idx_out))
+        return fail(QSA_E_INVALID, "logits, ctx_lens and idx_out must be non-NULL");
+    if (k > 2048) return fail(QSA_E_UNSUPPORTED, "k = %d (built: 1..2048)", k);
+    if (qsa::topk_groups_for_width(width) == 0)
+        return fail(QSA_E_UNSUPPORTED, "width = %d (built: up to 69632)", width);
+    if ((int64_t)num_rows * stride > kMaxBytes / 4) return fail(QSA_E_RANGE, "num_rows * logits_stride too large");
+    if (num_rows > 0 && !aligned16(logits)) return fail(QSA_E_ALIGN, "logits must be 16-byte aligned");
+    if (num_rows > 0 && stride % 4 != 0) return fail(QSA_E_ALIGN, "logits_stride must be a multiple of 4");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_paged_logits_check(const void *q, const float *w, const void *kcache, const float *kscale,
+                                  const int32_t *block_table, const int32_t *ctx_lens,
+                                  const int32_t *row_to_req, const float *out, const qsa_logits_shape *shape) {
+    return check_logits(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, shape);
+}
+
+qsa_status qsa_paged_logits(const void *q, const float *w, const void *kcache, const float *kscale,
+                            const int32_t *block_table, const int32_t *ctx_lens, const int32_t *row_to_req,
+                            float *out, const qsa_logits_shape *s, void *stream) {
+    qsa_status st = check_logits(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s);
+    if (st != QSA_OK) return st;
+    if (s->num_rows == 0 || s->width == 0) return ok();
+    const bool fp8 = s->k_dtype == QSA_FP8_E4M3FN;
+    const int64_t elt = fp8 ? 1 : 2;
+    qsa::LogitsPlan plan = qsa::plan_logits(fp8 ? 1 : 0, s->num_heads, s->num_rows, s->width);
+    qsa::LogitsArgs a = {};
+    a.q = q;
+    a.w = w;
+    a.kcache = static_cast<const uint8_t *>(kcache);
+    a.kscale = kscale;
+    a.block_table = block_table;
+    a.ctx_lens = ctx_lens;
+    a.row_to_req = row_to_req;
+    a.out = out;
+    a.num_rows = s->num_rows;
+    a.num_heads = s->num_heads;
+    a.block_size = s->block_size;
+    a.num_reqs = s->num_reqs;
+    a.max_blocks = s->max_blocks;
+    a.width = s->width;
+    const int64_t table_cols = (int64_t)s->max_blocks * s->block_size;
+    a.cap = (int32_t)(table_cols < s->width ? table_cols : s->width);
+    a.num_row_tiles = (s->num_rows + plan.rows_per_tile - 1) / plan.rows_per_tile;
+    const int chunk_cols = 16 * plan.tiles_per_prog;
+    a.num_chunks = (s->width + chunk_cols - 1) / chunk_cols;
+    if ((int64_t)a.num_row_tiles * a.num_chunks > 0x7FFFFFFF)
+        return fail(QSA_E_RANGE, "grid too large (%d row tiles x %d chunks)", a.num_row_tiles, a.num_chunks);
+    a.dtype = fp8 ? 1 : 0;
+    a.layout = s->kv_layout;
+    a.num_blocks = s->num_blocks;
+    a.out_stride = s->out_stride;
+    a.key_stride = s->head_dim * elt;
+    a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout == QSA_KV_COPACKED ? 4 * s->block_size : 0);
+    a.scale_offset = (int64_t)s->block_size * a.key_stride;
+    hipError_t e = qsa::launch_paged_logits(a, plan, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
+                          int32_t width, int32_t k, const int32_t *idx_out) {
+    return check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out);
+}
+
+qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
+                    int32_t width, int32_t k, int32_t *idx_out, void *stream) {
+    qsa_status st = check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out);
+    if (st != QSA_OK) return st;
+    if (num_rows == 0) return ok();
+    qsa::TopkArgs a = {logits, logits_stride, ctx_lens, num_rows, width, k, idx_out};
+    hipError_t e = qsa::launch_topk(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char *qsa_last_error(void) { return g_err; }
+
+const char *qsa_version(void) { return "qsaidx 0.1.0 gfx950"; }
+
+}  // extern "C"

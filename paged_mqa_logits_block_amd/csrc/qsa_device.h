@@ -1,0 +1,100 @@
+// Device-side helpers shared by the gfx950 kernels of libqsaidx.
+//
+// Wave64 primitives (ballot, lane masks, readlane), the MFMA vector types and
+// the order-preserving float key used by the selection kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
+}
+
+// number of set bits of `mask` below the calling lane
+__device__ __forceinline__ int mask_prefix(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+    return __builtin_amdgcn_ballot_w64(p);
+}
+
+__device__ __forceinline__ int readlane(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// value of `v` held by lane (lane_id ^ m); m < 64
+__device__ __forceinline__ float xor_lane_f(float v, int m) {
+    int src = (lane_id() ^ m) << 2;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+}
+
+__device__ __forceinline__ int xor_lane_i(int v, int m) {
+    int src = (lane_id() ^ m) << 2;
+    return __builtin_amdgcn_ds_bpermute(src, v);
+}
+
+// value of `v` held by lane `src` (any lane)
+__device__ __forceinline__ int shfl_i(int v, int src) {
+    return __builtin_amdgcn_ds_bpermute(src << 2, v);
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) v = max(v, xor_lane_i(v, m));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) v += xor_lane_i(v, m);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, xor_lane_f(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_min_f(float v) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) v = fminf(v, xor_lane_f(v, m));
+    return v;
+}
+
+// inclusive prefix sum across the wave
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int u = shfl_i(v, l >= d ? l - d : l);
+        if (l >= d) v += u;
+    }
+    return v;
+}
+
+// f32 bits -> u32 whose unsigned order is the float order; -0 is folded onto +0
+// so that the two zeros compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = (u == 0x80000000u) ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace qsa

@@ -1,0 +1,61 @@
+// Host/device interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Launch description of one qsa_paged_logits call, fully resolved on the host.
+struct LogitsArgs {
+    const void *q;
+    const float *w;
+    const uint8_t *kcache;
+    const float *kscale;
+    const int32_t *block_table;
+    const int32_t *ctx_lens;
+    const int32_t *row_to_req;
+    float *out;
+    int32_t num_rows;
+    int32_t num_heads;
+    int32_t block_size;
+    int32_t num_reqs;
+    int32_t max_blocks;
+    int32_t width;
+    int32_t cap;            // min(width, max_blocks * block_size)
+    int32_t num_row_tiles;  // ceil(num_rows / rows per tile)
+    int32_t num_chunks;     // column chunks per row tile
+    int32_t dtype;          // 0 bf16, 1 fp8 e4m3fn
+    int32_t layout;         // 0 paged, 1 co-packed
+    int32_t pad_;
+    int64_t num_blocks;
+    int64_t out_stride;
+    int64_t block_bytes;    // stride between pool blocks
+    int64_t key_stride;     // bytes between keys inside a block
+    int64_t scale_offset;   // co-packed: byte offset of the scales inside a block
+};
+
+// Variant chosen for a call: rows per tile and column tiles per program.
+struct LogitsPlan {
+    int rows_per_tile;
+    int tiles_per_prog;  // 16-column tiles per program
+    int m_tiles;         // 16-row MFMA tiles stacked per program
+};
+
+LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width);
+hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s);
+
+struct TopkArgs {
+    const float *logits;
+    int64_t stride;
+    const int32_t *ctx_lens;
+    int32_t num_rows;
+    int32_t width;
+    int32_t k;
+    int32_t *idx_out;
+};
+
+int topk_groups_for_width(int width);  // float4 groups per thread, 0 if too wide
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+}  // namespace qsa

@@ -1,0 +1,121 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and validates host arguments exactly as documented -- through the
+*_check entry points, which make no HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsaidx.h")
+
+m = pytest.importorskip("paged_mqa_logits_block_amd")
+
+A = 0x10000  # a 16-byte aligned stand-in address (never dereferenced)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"QSA_API\s+[\w\s\*]*?\b(qsa_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    syms = declared_symbols()
+    assert set(syms) == set(m.EXPORTED), syms
+    for s in syms:
+        assert hasattr(m.lib, s), s
+        assert ctypes.cast(getattr(m.lib, s), ctypes.c_void_p).value
+
+
+def test_version():
+    assert m.version().startswith("qsaidx ")
+    assert "gfx950" in m.version()
+
+
+def shape(**kw):
+    base = dict(num_rows=8, num_heads=4, head_dim=128, block_size=16, num_reqs=2, max_blocks=188,
+                width=3008, q_dtype=m.BF16, k_dtype=m.BF16, kv_layout=m.KV_PAGED, num_blocks=256,
+                out_stride=3008)
+    base.update(kw)
+    return m.LogitsShape(**base)
+
+
+def chk(s, q=A, w=None, kc=A, ks=None, bt=A, ctx=A, r2r=A, out=A):
+    return m.paged_logits_check(q, w, kc, ks, bt, ctx, r2r, out, s)
+
+
+def test_logits_valid_configurations():
+    assert chk(shape()) == m.OK
+    assert chk(shape(q_dtype=m.FP8_E4M3FN, k_dtype=m.FP8_E4M3FN, kv_layout=m.KV_COPACKED,
+                     num_heads=64, block_size=64)) == m.OK
+    assert chk(shape(q_dtype=m.FP8_E4M3FN, k_dtype=m.FP8_E4M3FN), ks=A) == m.OK
+    for H in (1, 2, 4, 8, 16, 32, 64):
+        assert chk(shape(num_heads=H)) == m.OK
+    for B in (16, 32, 48, 64, 400, 1024):
+        assert chk(shape(block_size=B)) == m.OK
+    # empty calls are valid whatever the pointers
+    assert chk(shape(num_rows=0), q=None, bt=None, ctx=None, r2r=None, out=None, kc=None) == m.OK
+    assert chk(shape(width=0, out_stride=1), out=A + 4) == m.OK
+    assert m.last_error() == ""
+
+
+@pytest.mark.parametrize("kw,ptrs,status", [
+    (dict(num_rows=-1), {}, m.E_INVALID),
+    (dict(width=-5), {}, m.E_INVALID),
+    (dict(num_heads=0), {}, m.E_INVALID),
+    (dict(block_size=0), {}, m.E_INVALID),
+    (dict(num_blocks=0), {}, m.E_INVALID),
+    (dict(out_stride=3000), {}, m.E_INVALID),
+    ({}, dict(q=None), m.E_INVALID),
+    ({}, dict(out=None), m.E_INVALID),
+    ({}, dict(r2r=None), m.E_INVALID),
+    (dict(q_dtype=m.FP8_E4M3FN), {}, m.E_DTYPE),  # mixed operand dtypes
+    (dict(k_dtype=7, q_dtype=7), {}, m.E_DTYPE),
+    (dict(kv_layout=9), {}, m.E_INVALID),
+    (dict(kv_layout=m.KV_COPACKED), {}, m.E_UNSUPPORTED),  # co-packed bf16
+    ({}, dict(ks=A), m.E_INVALID),  # a scale with bf16 keys
+    (dict(head_dim=64), {}, m.E_UNSUPPORTED),
+    (dict(num_heads=3), {}, m.E_UNSUPPORTED),
+    (dict(num_heads=128), {}, m.E_UNSUPPORTED),
+    (dict(block_size=8), {}, m.E_UNSUPPORTED),
+    (dict(block_size=200), {}, m.E_UNSUPPORTED),
+    (dict(block_size=2048), {}, m.E_UNSUPPORTED),
+    (dict(width=(1 << 24) + 16, out_stride=(1 << 24) + 16), {}, m.E_RANGE),
+    (dict(num_blocks=1 << 51), {}, m.E_RANGE),
+    ({}, dict(q=A + 4), m.E_ALIGN),
+    ({}, dict(kc=A + 8), m.E_ALIGN),
+    ({}, dict(out=A + 4), m.E_ALIGN),
+    (dict(out_stride=3010), {}, m.E_ALIGN),
+])
+def test_logits_rejections(kw, ptrs, status):
+    st = chk(shape(**kw), **ptrs)
+    assert st == status, (st, m.last_error())
+    assert m.last_error()
+
+
+def test_shape_null():
+    assert m.lib.qsa_paged_logits_check(A, None, A, None, A, A, A, A, None) == m.E_INVALID
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 3008, A, 8, 3008, 256, A), m.OK),
+    ((A, 69632, A, 8, 69632, 2048, A), m.OK),
+    ((A, 3008, A, 8, 3008, 1, A), m.OK),
+    ((None, 16, None, 0, 16, 8, None), m.OK),
+    ((A, 3008, A, -1, 3008, 256, A), m.E_INVALID),
+    ((A, 3008, A, 8, -1, 256, A), m.E_INVALID),
+    ((A, 3008, A, 8, 3008, 0, A), m.E_INVALID),
+    ((A, 3000, A, 8, 3008, 256, A), m.E_INVALID),
+    ((None, 3008, A, 8, 3008, 256, A), m.E_INVALID),
+    ((A, 3008, A, 8, 3008, 256, None), m.E_INVALID),
+    ((A, 3008, A, 8, 3008, 2049, A), m.E_UNSUPPORTED),
+    ((A, 69636, A, 8, 69636, 256, A), m.E_UNSUPPORTED),
+    ((A + 4, 3008, A, 8, 3008, 256, A), m.E_ALIGN),
+    ((A, 3010, A, 8, 3008, 256, A), m.E_ALIGN),
+])
+def test_topk_validation(args, status):
+    st = m.topk_check(*args)
+    assert st == status, (st, m.last_error())

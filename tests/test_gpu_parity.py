@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case prints what it runs before the first launch, so a failing run names
+its case.  Inputs come from qsa_inputs (seeded); expected values only from the
+oracle.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import qsa_inputs
+from gpu_helpers import (assert_logits_match, assert_topk_banded, assert_topk_exact, gpu_logits,
+                         gpu_topk, topk_tol)
+from qsa_inputs.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_mqa_logits_block_amd as m
+    say("library", m.version(), "device", torch.cuda.get_device_name(0))
+    return m
+
+
+def run_logits(inp, **kw):
+    dev = to_device(inp)
+    g = gpu_logits(inp, dev, **kw)
+    torch.cuda.synchronize()
+    return dev, g
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+SAMPLED_ROWS = {"prefill_chunk": [0, 1, 2, 3, 1000, 4095, 4096, 8191, 12000, 16380, 16381, 16382, 16383]}
+
+
+@pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES)
+def test_config_logits_and_topk(name):
+    inp = qsa_inputs.make_config(name, poison=True)
+    rows = SAMPLED_ROWS.get(name)
+    say(name, "rows", inp.num_rows, "width", inp.width, "H", inp.num_heads, inp.dtype, inp.layout)
+    dev, g = run_logits(inp)
+    sel = list(range(inp.num_rows)) if rows is None else rows
+    o = oracle.paged_logits(inp, rows=sel)
+    gl = g[torch.tensor(sel, device="cuda")].cpu().numpy()
+    assert_logits_match(gl, o, inp, sel, label=name)
+
+    # top-k on the GPU's own logits, end to end, against the oracle's selection
+    gi = gpu_topk(g, dev.ctx_lens, inp.topk)[torch.tensor(sel, device="cuda")].cpu().numpy()
+    o32 = o.astype(np.float32)
+    oi = oracle.topk(o32, inp.ctx_lens[sel], inp.topk)
+    assert_topk_banded(gi, oi, o, topk_tol(inp), label=name)
+
+    # top-k on identical logits (the oracle's, uploaded): exact
+    lt = torch.from_numpy(np.ascontiguousarray(o32)).cuda()
+    ct = torch.from_numpy(inp.ctx_lens[sel].astype(np.int32)).cuda()
+    gi2 = gpu_topk(lt, ct, inp.topk).cpu().numpy()
+    assert_topk_exact(gi2, oi, label=name)
+    # ascending column order, -1 padding after the selection
+    for r in range(gi2.shape[0]):
+        v = gi2[r][gi2[r] >= 0]
+        assert np.all(np.diff(v) > 0)
+        assert np.all(gi2[r][len(v):] == -1)
+
+
+# ---------------------------------------------------------------------------
+# logits edge cases
+# ---------------------------------------------------------------------------
+
+EDGE_CTX = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1000]
+
+
+@pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("dtype,layout", [("bf16", "paged"), ("fp8", "paged"), ("fp8", "copacked")])
+def test_heads_and_dtypes(H, dtype, layout):
+    ctx = [EDGE_CTX[(i * 5 + H) % len(EDGE_CTX)] for i in range(6)]
+    inp = qsa_inputs.build(name="edge", seed=100 + H, req_rows=[2, 1, 3], ctx_rows=ctx,
+                           num_heads=H, block_size=16 if H < 16 else 64, dtype=dtype,
+                           layout=layout, weights=(H % 2 == 0), poison=True)
+    say("heads", H, dtype, layout, "ctx", ctx)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"H{H}")
+
+
+@pytest.mark.parametrize("B", [16, 32, 64, 128, 1024])
+def test_block_sizes_and_ragged_ctx(B):
+    ctx = [1, B - 1, B, B + 1, 3 * B + 5, 2047, 2048, 2049]
+    inp = qsa_inputs.build(name="blk", seed=200 + B, req_rows=[4, 4], ctx_rows=ctx, num_heads=4,
+                           block_size=B, poison=True)
+    say("block", B, "ctx", ctx)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"B{B}")
+
+
+def test_rows_spanning_requests_and_shuffled():
+    # one row per request, and rows of one request scattered over tiles
+    ctx = list(range(100, 100 + 37 * 13, 13))
+    inp = qsa_inputs.build(name="span", seed=301, req_rows=[1] * 37, ctx_rows=ctx, num_heads=4,
+                           block_size=16, weights=True, poison=True)
+    say("spanning", len(ctx))
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label="span")
+    inp2 = qsa_inputs.build(name="shuf", seed=302, req_rows=[3, 5, 2, 6], ctx_rows=[40 + 9 * i for i in range(16)],
+                            num_heads=4, block_size=16, shuffle_rows=True, poison=True)
+    say("shuffled rows")
+    _, g2 = run_logits(inp2)
+    assert_logits_match(g2.cpu().numpy(), oracle.paged_logits(inp2), inp2, label="shuf")
+
+
+def test_ctx_clamping_and_width():
+    # ctx beyond the table, beyond the width, and negative
+    inp = qsa_inputs.build(name="clamp", seed=401, req_rows=[2, 2], ctx_rows=[5000, 70, -3, 64],
+                           kv_lens=[64, 64], num_heads=4, block_size=16, max_blocks=4, width=50,
+                           poison=True)
+    say("clamp")
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label="clamp")
+
+
+def test_untouched_stride_tail_and_nan_canaries():
+    inp = qsa_inputs.make_config("tiny", poison=True)
+    dev = to_device(inp)
+    stride = inp.width + 52
+    buf = torch.full((inp.num_rows, stride), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[:, : inp.width]
+    say("stride tail")
+    gpu_logits(inp, dev, out=out)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(np.isnan(b[:, inp.width:]))
+    assert_logits_match(b[:, : inp.width], oracle.paged_logits(inp), inp, label="stride")
+
+
+def test_block_table_permutation_bitwise():
+    inp = qsa_inputs.make_config("tiny")
+    say("permutation")
+    _, g1 = run_logits(inp)
+    perm = np.random.default_rng(5).permutation(inp.num_blocks)
+    inv = np.argsort(perm)
+    inp.kcache = inp.kcache[inv]
+    inp.block_table = perm[inp.block_table].astype(np.int32)
+    _, g2 = run_logits(inp)
+    assert torch.equal(g1, g2)
+
+
+def test_repeat_launch_deterministic():
+    inp = qsa_inputs.make_config("tiny")
+    dev = to_device(inp)
+    say("repeat")
+    a = gpu_logits(inp, dev).clone()
+    b = gpu_logits(inp, dev)
+    ta = gpu_topk(a, dev.ctx_lens, 256).clone()
+    tb = gpu_topk(b, dev.ctx_lens, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ta, tb)
+
+
+def test_invalid_table_entry_and_request_give_nan():
+    inp = qsa_inputs.build(name="bad", seed=501, req_rows=[2, 2], ctx_rows=[40, 40, 40, 40],
+                           num_heads=4, block_size=16)
+    inp.block_table[0, 1] = inp.num_blocks + 7  # columns 16..31 of request 0
+    inp.row_to_req = np.array([0, 0, 9, 1], dtype=np.int32)  # row 2 points past the table
+    say("invalid table entry / request")
+    _, g = run_logits(inp)
+    x = g.cpu().numpy()
+    assert np.all(np.isnan(x[0:2, 16:32])) and np.all(np.isfinite(x[0:2, :16]))
+    assert np.all(np.isfinite(x[0:2, 32:40]))
+    assert np.all(np.isnan(x[2, :40])) and np.all(x[2, 40:] == -np.inf)
+    assert np.all(np.isfinite(x[3, :40]))
+
+
+def test_empty_inputs():
+    m = pytest.importorskip("paged_mqa_logits_block_amd")
+    inp = qsa_inputs.make_config("tiny")
+    dev = to_device(inp)
+    say("empty")
+    out = m.paged_logits(dev.q[:0], dev.kcache, dev.block_table, dev.ctx_lens[:0], dev.row_to_req[:0],
+                         width=inp.width, block_size=16)
+    assert out.shape == (0, inp.width)
+    out2 = m.paged_logits(dev.q, dev.kcache, dev.block_table, dev.ctx_lens, dev.row_to_req,
+                          width=0, block_size=16)
+    assert out2.shape == (inp.num_rows, 0)
+    lt = torch.zeros((0, 16), dtype=torch.float32, device="cuda")
+    assert m.topk(lt, torch.zeros(0, dtype=torch.int32, device="cuda"), 8).shape == (0, 8)
+
+
+# ---------------------------------------------------------------------------
+# top-k edge cases (identical logits on both sides: exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["normal", "ints", "const", "zeros", "relu"])
+@pytest.mark.parametrize("k", [1, 7, 256, 2048])
+def test_topk_distributions(kind, k):
+    W = 9000
+    ctx = [0, 1, k - 1 if k > 1 else 0, k, k + 1, 3000, 8999, 9000, 12000, 4097]
+    x = qsa_inputs.make_logits(len(ctx), W, ctx, seed=k * 7 + len(kind), kind=kind, tail="nan")
+    say("topk", kind, k)
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    gi = gpu_topk(xt, ct, k).cpu().numpy()
+    ctx_np = np.minimum(np.maximum(np.array(ctx), 0), W)
+    xo = x.copy()
+    for r, c in enumerate(ctx_np):
+        xo[r, c:] = -np.inf  # the oracle refuses NaN; the tail is never read
+    oi = oracle.topk(xo, ctx_np, k)
+    assert_topk_exact(gi, oi, label=f"{kind}/k{k}")
+
+
+@pytest.mark.parametrize("W", [69632, 65600, 32768, 4096, 4099])
+def test_topk_widths_and_large_tie_buckets(W):
+    # const rows put everything in one bucket (larger than the LDS list);
+    # ints rows make large tie groups inside the list
+    rows = []
+    for kind in ("const", "ints", "normal"):
+        rows.append(qsa_inputs.make_logits(2, W, [W, W - 3], seed=W % 97, kind=kind))
+    x = np.concatenate(rows)
+    ctx = np.array([W, W - 3] * 3)
+    say("topk width", W)
+    gi = gpu_topk(torch.from_numpy(x).cuda(), torch.from_numpy(ctx.astype(np.int32)).cuda(), 2048).cpu().numpy()
+    oi = oracle.topk(x, ctx, 2048)
+    assert_topk_exact(gi, oi, label=f"W{W}")
+
+
+def test_topk_padded_row_stride():
+    W, stride = 5000, 5012
+    x = qsa_inputs.make_logits(3, stride, [5000, 4000, 2500], seed=9, kind="normal", tail="nan")
+    say("topk stride")
+    xt = torch.from_numpy(x).cuda()[:, :W]
+    ct = torch.tensor([5000, 4000, 2500], dtype=torch.int32, device="cuda")
+    gi = gpu_topk(xt, ct, 2048, width=W).cpu().numpy()
+    xo = x[:, :W].copy()
+    xo[1, 4000:] = -np.inf
+    xo[2, 2500:] = -np.inf
+    oi = oracle.topk(xo, [5000, 4000, 2500], 2048)
+    assert_topk_exact(gi, oi, label="stride")
