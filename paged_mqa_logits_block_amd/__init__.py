@@ -46,6 +46,12 @@ class LogitsShape(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime under the same soname as /opt/rocm's.
+    # Importing torch first makes libqsaidx bind to that one runtime, which
+    # also owns the device allocations and stream handles passed in; loading
+    # the library first would start a second runtime in the process.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")

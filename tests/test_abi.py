@@ -119,3 +119,11 @@ def test_shape_null():
 def test_topk_validation(args, status):
     st = m.topk_check(*args)
     assert st == status, (st, m.last_error())
+
+
+def test_one_hip_runtime_in_process():
+    """The binding must share torch's HIP runtime (streams and allocations are
+    torch's); a second copy of libamdhip64 in the process breaks launches."""
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
+    assert len(libs) == 1, libs

@@ -129,8 +129,18 @@ def test_ctx_clamping_and_width():
                            kv_lens=[64, 64], num_heads=4, block_size=16, max_blocks=4, width=50,
                            poison=True)
     say("clamp")
-    _, g = run_logits(inp)
-    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label="clamp")
+    dev = to_device(inp)
+    # a ragged width needs a row stride padded to a multiple of 4 floats
+    buf = torch.full((inp.num_rows, 52), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_logits(inp, dev, out=buf[:, :50])
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(np.isnan(b[:, 50:]))
+    assert_logits_match(b[:, :50], oracle.paged_logits(inp), inp, label="clamp")
+    m = pytest.importorskip("paged_mqa_logits_block_amd")
+    with pytest.raises(m.QsaError) as e:
+        gpu_logits(inp, dev)  # unpadded stride 50
+    assert e.value.status == m.E_ALIGN
 
 
 def test_untouched_stride_tail_and_nan_canaries():
@@ -232,7 +242,10 @@ def test_topk_widths_and_large_tie_buckets(W):
     x = np.concatenate(rows)
     ctx = np.array([W, W - 3] * 3)
     say("topk width", W)
-    gi = gpu_topk(torch.from_numpy(x).cuda(), torch.from_numpy(ctx.astype(np.int32)).cuda(), 2048).cpu().numpy()
+    stride = (W + 3) // 4 * 4  # rows padded to a multiple of 4 floats
+    xt = torch.full((x.shape[0], stride), float("nan"), dtype=torch.float32, device="cuda")
+    xt[:, :W] = torch.from_numpy(x).cuda()
+    gi = gpu_topk(xt[:, :W], torch.from_numpy(ctx.astype(np.int32)).cuda(), 2048, width=W).cpu().numpy()
     oi = oracle.topk(x, ctx, 2048)
     assert_topk_exact(gi, oi, label=f"W{W}")
 
