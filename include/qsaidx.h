@@ -123,6 +123,17 @@ QSA_API qsa_status qsa_paged_logits(const void *q, const float *w, const void *k
                             const int32_t *ctx_lens, const int32_t *row_to_req, float *out,
                             const qsa_logits_shape *shape, void *stream);
 
+/* qsa_paged_logits, with the kernel timed: start_event / stop_event (hipEvent_t
+ * created by the caller, or NULL) are recorded by the dispatch itself at the
+ * kernel's start and end, so hipEventElapsedTime gives the kernel's duration
+ * without marker-packet overhead.  For measurement tools; otherwise identical.
+ * When the call launches nothing (R = 0 or W = 0) the events are not touched. */
+QSA_API qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kcache,
+                                          const float *kscale, const int32_t *block_table,
+                                          const int32_t *ctx_lens, const int32_t *row_to_req,
+                                          float *out, const qsa_logits_shape *shape, void *stream,
+                                          void *start_event, void *stop_event);
+
 /* Validation of qsa_paged_logits' host-visible arguments only: no HIP call, no
  * launch.  Returns what qsa_paged_logits would return before launching. */
 QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const void *kcache,
@@ -150,6 +161,12 @@ QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const v
  */
 QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
                     int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out, void *stream);
+
+/* qsa_topk with the kernel timed by dispatch-recorded events (as
+ * qsa_paged_logits_timed). */
+QSA_API qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                                  int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out,
+                                  void *stream, void *start_event, void *stop_event);
 
 /* Validation of qsa_topk's host-visible arguments only: no HIP call, no launch. */
 QSA_API qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,

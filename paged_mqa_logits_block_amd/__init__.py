@@ -24,8 +24,8 @@ STATUS_NAMES = {0: "QSA_OK", 1: "QSA_E_INVALID", 2: "QSA_E_DTYPE", 3: "QSA_E_UNS
 BF16, FP8_E4M3FN = 0, 1
 KV_PAGED, KV_COPACKED = 0, 1
 
-EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_check", "qsa_topk", "qsa_topk_check",
-            "qsa_last_error", "qsa_version")
+EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
+            "qsa_topk_timed", "qsa_topk_check", "qsa_last_error", "qsa_version")
 
 
 class QsaError(RuntimeError):
@@ -60,10 +60,14 @@ def _load():
     sp = ctypes.POINTER(LogitsShape)
     lib.qsa_paged_logits.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp, vp]
     lib.qsa_paged_logits.restype = ctypes.c_int
+    lib.qsa_paged_logits_timed.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp, vp, vp, vp]
+    lib.qsa_paged_logits_timed.restype = ctypes.c_int
     lib.qsa_paged_logits_check.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp]
     lib.qsa_paged_logits_check.restype = ctypes.c_int
     lib.qsa_topk.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp]
     lib.qsa_topk.restype = ctypes.c_int
+    lib.qsa_topk_timed.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, vp, vp]
+    lib.qsa_topk_timed.restype = ctypes.c_int
     lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32, i32, i32, i32p]
     lib.qsa_topk_check.restype = ctypes.c_int
     lib.qsa_last_error.argtypes = []
@@ -126,10 +130,17 @@ def make_shape(q, kcache, block_table, *, width: int, block_size: int, layout: i
         out_stride=int(width if out_stride is None else out_stride))
 
 
+def _event(e) -> Optional[int]:
+    """hipEvent_t of a torch.cuda.Event (created on its first record)."""
+    return None if e is None else int(e.cuda_event)
+
+
 def paged_logits(q, kcache, block_table, ctx_lens, row_to_req, *, width: int, block_size: int,
-                 w=None, kscale=None, layout: int = KV_PAGED, out=None, stream=None):
+                 w=None, kscale=None, layout: int = KV_PAGED, out=None, stream=None, events=None):
     """``qsa_paged_logits``: f32 logits ``[R, width]`` (or into ``out``, whose row
-    stride may exceed ``width``).  See include/qsaidx.h for the contract."""
+    stride may exceed ``width``).  See include/qsaidx.h for the contract.
+    ``events=(start, stop)`` (recorded torch.cuda.Event objects) routes the call
+    through ``qsa_paged_logits_timed``."""
     import torch
     for name, t in (("q", q), ("kcache", kcache), ("block_table", block_table),
                     ("ctx_lens", ctx_lens), ("row_to_req", row_to_req), ("w", w), ("kscale", kscale)):
@@ -150,14 +161,17 @@ def paged_logits(q, kcache, block_table, ctx_lens, row_to_req, *, width: int, bl
     _require(out.dtype == torch.float32 and out.dim() == 2 and out.stride(1) == 1, "out must be f32 [R, >=width]")
     shape = make_shape(q, kcache, block_table, width=width, block_size=block_size, layout=layout,
                        out_stride=out.stride(0) if R > 0 else width)
-    st = lib.qsa_paged_logits(_ptr(q), _ptr(w), _ptr(kcache), _ptr(kscale), _ptr(block_table),
-                              _ptr(ctx_lens), _ptr(row_to_req), _ptr(out), ctypes.byref(shape),
-                              _stream(stream))
+    args = (_ptr(q), _ptr(w), _ptr(kcache), _ptr(kscale), _ptr(block_table), _ptr(ctx_lens),
+            _ptr(row_to_req), _ptr(out), ctypes.byref(shape), _stream(stream))
+    if events is None:
+        st = lib.qsa_paged_logits(*args)
+    else:
+        st = lib.qsa_paged_logits_timed(*args, _event(events[0]), _event(events[1]))
     _raise_on(st)
     return out
 
 
-def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, stream=None):
+def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, stream=None, events=None):
     """``qsa_topk``: int32 ``[R, k]`` selected columns, ascending, -1 padded."""
     import torch
     _require(logits.is_cuda and ctx_lens.is_cuda, "logits and ctx_lens must be device tensors")
@@ -171,7 +185,11 @@ def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, str
     _require(out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (R, k),
              "out must be contiguous int32 [R, k]")
     stride = int(logits.stride(0)) if R > 0 else width
-    st = lib.qsa_topk(_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), _stream(stream))
+    args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), _stream(stream))
+    if events is None:
+        st = lib.qsa_topk(*args)
+    else:
+        st = lib.qsa_topk_timed(*args, _event(events[0]), _event(events[1]))
     _raise_on(st)
     return out
 
@@ -186,3 +204,55 @@ def paged_logits_check(q_ptr, w_ptr, kcache_ptr, kscale_ptr, bt_ptr, ctx_ptr, r2
 def topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr) -> int:
     """Host-side validation only (``qsa_topk_check``); pointers are ints."""
     return lib.qsa_topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr)
+
+
+class PreparedLogits:
+    """A validated ``qsa_paged_logits`` call on fixed tensors: construction does
+    every check once; each call only crosses the C ABI (for tight loops and
+    benchmarks).  The tensors must stay alive and unchanged in shape."""
+
+    def __init__(self, q, kcache, block_table, ctx_lens, row_to_req, out, *, width: int,
+                 block_size: int, w=None, kscale=None, layout: int = KV_PAGED, stream=None):
+        # one full checked call path on the host side, without launching
+        R = int(q.shape[0])
+        _require(out.dtype.is_floating_point and out.dim() == 2 and out.stride(1) == 1,
+                 "out must be f32 [R, >=width]")
+        self.shape = make_shape(q, kcache, block_table, width=width, block_size=block_size,
+                                layout=layout, out_stride=out.stride(0) if R > 0 else width)
+        self._keep = (q, kcache, block_table, ctx_lens, row_to_req, out, w, kscale)
+        self._args = (_ptr(q), _ptr(w), _ptr(kcache), _ptr(kscale), _ptr(block_table),
+                      _ptr(ctx_lens), _ptr(row_to_req), _ptr(out), ctypes.byref(self.shape),
+                      _stream(stream))
+        _raise_on(lib.qsa_paged_logits_check(*self._args[:9]))
+        self.out = out
+
+    def __call__(self, events=None):
+        if events is None:
+            st = lib.qsa_paged_logits(*self._args)
+        else:
+            st = lib.qsa_paged_logits_timed(*self._args, _event(events[0]), _event(events[1]))
+        if st != OK:
+            _raise_on(st)
+        return self.out
+
+
+class PreparedTopk:
+    """A validated ``qsa_topk`` call on fixed tensors (see PreparedLogits)."""
+
+    def __init__(self, logits, ctx_lens, k: int, out, *, width: Optional[int] = None, stream=None):
+        R = int(logits.shape[0])
+        width = int(logits.shape[1]) if width is None else int(width)
+        stride = int(logits.stride(0)) if R > 0 else width
+        self._keep = (logits, ctx_lens, out)
+        self._args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), _stream(stream))
+        _raise_on(lib.qsa_topk_check(*self._args[:7]))
+        self.out = out
+
+    def __call__(self, events=None):
+        if events is None:
+            st = lib.qsa_topk(*self._args)
+        else:
+            st = lib.qsa_topk_timed(*self._args, _event(events[0]), _event(events[1]))
+        if st != OK:
+            _raise_on(st)
+        return self.out

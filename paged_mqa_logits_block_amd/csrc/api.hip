@@ -107,6 +107,14 @@ qsa_status qsa_paged_logits_check(const void *q, const float *w, const void *kca
 qsa_status qsa_paged_logits(const void *q, const float *w, const void *kcache, const float *kscale,
                             const int32_t *block_table, const int32_t *ctx_lens, const int32_t *row_to_req,
                             float *out, const qsa_logits_shape *s, void *stream) {
+    return qsa_paged_logits_timed(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s, stream,
+                                  nullptr, nullptr);
+}
+
+qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kcache, const float *kscale,
+                                  const int32_t *block_table, const int32_t *ctx_lens,
+                                  const int32_t *row_to_req, float *out, const qsa_logits_shape *s,
+                                  void *stream, void *start_event, void *stop_event) {
     qsa_status st = check_logits(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s);
     if (st != QSA_OK) return st;
     if (s->num_rows == 0 || s->width == 0) return ok();
@@ -142,7 +150,9 @@ qsa_status qsa_paged_logits(const void *q, const float *w, const void *kcache, c
     a.key_stride = s->head_dim * elt;
     a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout == QSA_KV_COPACKED ? 4 * s->block_size : 0);
     a.scale_offset = (int64_t)s->block_size * a.key_stride;
-    hipError_t e = qsa::launch_paged_logits(a, plan, static_cast<hipStream_t>(stream));
+    hipError_t e = qsa::launch_paged_logits(a, plan, static_cast<hipStream_t>(stream),
+                                            static_cast<hipEvent_t>(start_event),
+                                            static_cast<hipEvent_t>(stop_event));
     if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -154,11 +164,18 @@ qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int3
 
 qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
                     int32_t width, int32_t k, int32_t *idx_out, void *stream) {
+    return qsa_topk_timed(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, stream, nullptr, nullptr);
+}
+
+qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
+                          int32_t width, int32_t k, int32_t *idx_out, void *stream, void *start_event,
+                          void *stop_event) {
     qsa_status st = check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out);
     if (st != QSA_OK) return st;
     if (num_rows == 0) return ok();
     qsa::TopkArgs a = {logits, logits_stride, ctx_lens, num_rows, width, k, idx_out};
-    hipError_t e = qsa::launch_topk(a, static_cast<hipStream_t>(stream));
+    hipError_t e = qsa::launch_topk(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                                    static_cast<hipEvent_t>(stop_event));
     if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -255,35 +255,35 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
 }
 
 template <bool FP8, int H, int MT, int TPW>
-hipError_t launch_h(const LogitsArgs &a, hipStream_t s) {
+hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
     const bool has_s = FP8 && (a.layout == 1 || a.kscale != nullptr);
     if (has_w && has_s)
-        hipLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, true>), grid, block, 0, s, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, true>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)
-        hipLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, false>), grid, block, 0, s, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, false>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_s)
-        hipLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, true>), grid, block, 0, s, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, true>), grid, block, 0, s, e0, e1, 0, a);
     else
-        hipLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, false>), grid, block, 0, s, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, false>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
 }
 
 template <bool FP8>
-hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s) {
+hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int TPW = 4;
+    (void)p;
     switch (a.num_heads) {
-        case 1: return launch_h<FP8, 1, 1, TPW>(a, s);
-        case 2: return launch_h<FP8, 2, 1, TPW>(a, s);
-        case 4: return launch_h<FP8, 4, 1, TPW>(a, s);
-        case 8: return launch_h<FP8, 8, 1, TPW>(a, s);
-        case 16: return launch_h<FP8, 16, 1, TPW>(a, s);
-        case 32: return launch_h<FP8, 32, 2, TPW>(a, s);
-        case 64: return launch_h<FP8, 64, 4, TPW>(a, s);
+        case 1: return launch_h<FP8, 1, 1, TPW>(a, s, e0, e1);
+        case 2: return launch_h<FP8, 2, 1, TPW>(a, s, e0, e1);
+        case 4: return launch_h<FP8, 4, 1, TPW>(a, s, e0, e1);
+        case 8: return launch_h<FP8, 8, 1, TPW>(a, s, e0, e1);
+        case 16: return launch_h<FP8, 16, 1, TPW>(a, s, e0, e1);
+        case 32: return launch_h<FP8, 32, 2, TPW>(a, s, e0, e1);
+        case 64: return launch_h<FP8, 64, 4, TPW>(a, s, e0, e1);
         default: return hipErrorInvalidValue;
     }
-    (void)p;
 }
 
 }  // namespace
@@ -299,9 +299,10 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width) {
     return p;
 }
 
-hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s) {
+hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
     if (a.num_row_tiles == 0 || a.num_chunks == 0) return hipSuccess;
-    return a.dtype == 0 ? launch_dtype<false>(a, p, s) : launch_dtype<true>(a, p, s);
+    return a.dtype == 0 ? launch_dtype<false>(a, p, s, e0, e1) : launch_dtype<true>(a, p, s, e0, e1);
 }
 
 }  // namespace qsa

@@ -1,6 +1,7 @@
 // Host/device interface between the C-ABI layer and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,7 +44,10 @@ struct LogitsPlan {
 };
 
 LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width);
-hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s);
+// start / stop (may be null) are recorded by the dispatch packet itself at the
+// kernel's start and end.
+hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,
+                               hipEvent_t start, hipEvent_t stop);
 
 struct TopkArgs {
     const float *logits;
@@ -56,6 +60,6 @@ struct TopkArgs {
 };
 
 int topk_groups_for_width(int width);  // float4 groups per thread, 0 if too wide
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace qsa

@@ -262,3 +262,29 @@ def test_topk_padded_row_stride():
     xo[2, 2500:] = -np.inf
     oi = oracle.topk(xo, [5000, 4000, 2500], 2048)
     assert_topk_exact(gi, oi, label="stride")
+
+
+def test_prepared_and_timed_calls_match():
+    m = pytest.importorskip("paged_mqa_logits_block_amd")
+    inp = qsa_inputs.make_config("tiny")
+    dev = to_device(inp)
+    say("prepared / timed calls")
+    ref = gpu_logits(inp, dev).clone()
+    ref_idx = gpu_topk(ref, dev.ctx_lens, inp.topk).clone()
+    out = torch.full_like(ref, float("nan"))
+    idx = torch.full_like(ref_idx, -7)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    pl = m.PreparedLogits(dev.q, dev.kcache, dev.block_table, dev.ctx_lens, dev.row_to_req, out,
+                          width=inp.width, block_size=inp.block_size)
+    pt = m.PreparedTopk(out, dev.ctx_lens, inp.topk, idx)
+    pl((ev[0], ev[1]))
+    pt((ev[2], ev[3]))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(idx, ref_idx)
+    assert ev[0].elapsed_time(ev[1]) > 0 and ev[2].elapsed_time(ev[3]) > 0
+    pl()
+    pt()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(idx, ref_idx)
