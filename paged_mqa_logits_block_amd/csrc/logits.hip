@@ -100,15 +100,23 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     const int row0 = tile * RT;
     const int c0 = chunk * TPW * 16;
 
-    // per-row info: lane r < RT holds row row0 + r
-    const int my_row = row0 + l;
-    const bool my_valid = (l < RT) && (my_row < a.num_rows);
-    int my_ctx = 0, my_req = -1;
-    if (my_valid) {
-        my_ctx = min(max(a.ctx_lens[my_row], 0), a.cap);
-        my_req = a.row_to_req[my_row];
+    // per-row info of the tile, wave-uniform: every load issued before any use
+    // (indices clamped in bounds, padding rows masked afterwards)
+    int ctx_r[RT], req_r[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int row = min(row0 + r, a.num_rows - 1);
+        ctx_r[r] = a.ctx_lens[row];
+        req_r[r] = a.row_to_req[row];
     }
-    uint64_t todo = ballot(my_valid);
+    uint32_t todo = 0u;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const bool valid = row0 + r < a.num_rows;
+        ctx_r[r] = valid ? min(max(ctx_r[r], 0), a.cap) : 0;
+        req_r[r] = valid ? req_r[r] : -1;
+        todo |= (valid ? 1u : 0u) << r;
+    }
 
     // resident Q: the A operand of every stacked tile and K step;
     // stacked row m = 16*mt + (l % 16) is (tile row m / H, head m % H)
@@ -156,11 +164,21 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     const float qnan = __builtin_nanf("");
 
     while (todo) {
-        const int r0 = __builtin_ctzll(todo);
-        const int req = readlane(my_req, r0);
-        const uint64_t set = ballot(my_valid && my_req == req) & todo;
+        // the rows of one request: the lowest pending row's request
+        const int r0 = __builtin_ctz(todo);
+        int req = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) req = (r == r0) ? req_r[r] : req;
+        uint32_t set = 0u;
+        int vis = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (((todo >> r) & 1u) && req_r[r] == req) {
+                set |= 1u << r;
+                vis = max(vis, ctx_r[r]);
+            }
+        }
         todo &= ~set;
-        const int vis = wave_max_i(((set >> l) & 1) ? my_ctx : 0);
         // a row_to_req value outside the table is never dereferenced: its rows
         // read no keys and their visible columns are written as NaN
         const bool req_ok = req >= 0 && req < a.num_reqs;
@@ -171,58 +189,81 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         bool st_on[NR];
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            st_ctx[j] = shfl_i(my_ctx, st_rr[j]);
-            st_on[j] = st_lane[j] && ((set >> st_rr[j]) & 1);
+            int c = 0;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) c = (st_rr[j] == r) ? ctx_r[r] : c;
+            st_ctx[j] = c;
+            st_on[j] = st_lane[j] && ((set >> st_rr[j]) & 1u);
         }
 
+        // Keys of the chunk: all table entries, then all key tiles, issued
+        // before the first is used.  A tile that is past the visible range or
+        // whose table entry is out of range loads block 0 (always in the pool)
+        // and its scores are discarded.  A chunk entirely past the visible
+        // range loads nothing.
+        const bool any_live = c0 < vis;
+        typename F::T b[TPW][F::kSteps];
+        float kscale[TPW];
+        bool ok[TPW];
+        if (any_live) {
+            int blk[TPW];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                blk[t] = req_ok ? bt[min((c0 + 16 * t) / a.block_size, a.max_blocks - 1)] : -1;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int col0 = c0 + 16 * t;
+                ok[t] = col0 < vis && blk[t] >= 0 && (int64_t)blk[t] < a.num_blocks;
+                const int slot = (col0 % a.block_size) + (l & 15);
+                const int64_t boff = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
+                const uint8_t *kb = a.kcache + boff;
+                const uint8_t *krow = kb + (int64_t)(ok[t] ? slot : (l & 15)) * a.key_stride;
+#pragma unroll
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(krow, l, s);
+                kscale[t] = 1.0f;
+                if (HAS_SCALE) {
+                    if (a.layout == 1)
+                        kscale[t] = *reinterpret_cast<const float *>(kb + a.scale_offset + 4 * (ok[t] ? slot : 0));
+                    else
+                        kscale[t] = a.kscale[ok[t] ? (int64_t)blk[t] * a.block_size + slot : 0];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                ok[t] = false;
+                kscale[t] = 1.0f;
+#pragma unroll
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::zero();
+            }
+        }
+
+        // Scores of every tile first, stores after: on gfx9 the memory counter
+        // that orders a wait on loaded data also covers earlier stores, so a
+        // store between two tiles would hold the next tile until it lands.
+        float val[TPW][NR];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const int col0 = c0 + 16 * t;
-            if (col0 >= a.width) break;
             f32x4 acc[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bool bad = false;
-            float kscale = 1.0f;
-            const bool live = col0 < vis;
-            if (live) {
-                const int p = col0 / a.block_size;
-                const int slot = col0 - p * a.block_size + (l & 15);
-                const int blk = req_ok ? bt[p] : -1;
-                if (blk >= 0 && (int64_t)blk < a.num_blocks) {
-                    const uint8_t *kb = a.kcache + (int64_t)blk * a.block_bytes;
-                    const uint8_t *krow = kb + (int64_t)slot * a.key_stride;
-                    typename F::T b[F::kSteps];
 #pragma unroll
-                    for (int s = 0; s < F::kSteps; ++s) b[s] = F::load(krow, l, s);
-                    if (HAS_SCALE) {
-                        if (a.layout == 1)
-                            kscale = *reinterpret_cast<const float *>(kb + a.scale_offset + 4 * slot);
-                        else
-                            kscale = a.kscale[(int64_t)blk * a.block_size + slot];
-                    }
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int s = 0; s < F::kSteps; ++s) acc[mt] = F::mma(qa[mt][s], b[s], acc[mt]);
-                } else {
-                    bad = true;
-                }
-            }
+                for (int s = 0; s < F::kSteps; ++s) acc[mt] = F::mma(qa[mt][s], b[t][s], acc[mt]);
 
             // head reduction: per stored row, sum of w * ReLU over its heads
-            float val[NR];
             if (H <= 4) {
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
                     float v = 0.0f;
 #pragma unroll
                     for (int i = j * H; i < j * H + H; ++i) v += wv[0][i] * fmaxf(acc[0][i], 0.0f);
-                    val[j] = v;
+                    val[t][j] = v;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < NR; ++j) val[j] = 0.0f;
+                for (int j = 0; j < NR; ++j) val[t][j] = 0.0f;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     // all 4 slots of tile mt belong to tile row (16*mt + 4*g) / H
@@ -232,21 +273,26 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                     for (int i = 0; i < 4; ++i) c += wv[mt][i] * fmaxf(acc[mt][i], 0.0f);
 #pragma unroll
                     for (int j = 0; j < NR; ++j)
-                        if (j == rr) val[j] += c;
+                        if (j == rr) val[t][j] += c;
                 }
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
-                    if (H >= 8) val[j] += xor_lane_f(val[j], 16);
-                    if (H >= 16) val[j] += xor_lane_f(val[j], 32);
+                    if (H >= 8) val[t][j] += xor_lane_f(val[t][j], 16);
+                    if (H >= 16) val[t][j] += xor_lane_f(val[t][j], 32);
                 }
             }
+        }
 
-            // mask and store: lane writes column col of each row it stores
+        // mask and store: lane writes column col0 + l%16 of each row it stores
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int col0 = c0 + 16 * t;
+            const bool live = col0 < vis;
             const int col = col0 + (l & 15);
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
                 if (st_on[j] && col < a.width) {
-                    const float v = live ? (bad ? qnan : val[j] * kscale) : neg_inf;
+                    const float v = live ? (ok[t] ? val[t][j] * kscale[t] : qnan) : neg_inf;
                     a.out[(int64_t)(row0 + st_rr[j]) * a.out_stride + col] = col < st_ctx[j] ? v : neg_inf;
                 }
             }
@@ -272,16 +318,16 @@ hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_
 
 template <bool FP8>
 hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr int TPW = 4;
+    // chunk width per program (tiles of 16 columns) follows plan_logits
     (void)p;
     switch (a.num_heads) {
-        case 1: return launch_h<FP8, 1, 1, TPW>(a, s, e0, e1);
-        case 2: return launch_h<FP8, 2, 1, TPW>(a, s, e0, e1);
-        case 4: return launch_h<FP8, 4, 1, TPW>(a, s, e0, e1);
-        case 8: return launch_h<FP8, 8, 1, TPW>(a, s, e0, e1);
-        case 16: return launch_h<FP8, 16, 1, TPW>(a, s, e0, e1);
-        case 32: return launch_h<FP8, 32, 2, TPW>(a, s, e0, e1);
-        case 64: return launch_h<FP8, 64, 4, TPW>(a, s, e0, e1);
+        case 1: return launch_h<FP8, 1, 1, 4>(a, s, e0, e1);
+        case 2: return launch_h<FP8, 2, 1, 4>(a, s, e0, e1);
+        case 4: return launch_h<FP8, 4, 1, 4>(a, s, e0, e1);
+        case 8: return launch_h<FP8, 8, 1, 8>(a, s, e0, e1);
+        case 16: return launch_h<FP8, 16, 1, 8>(a, s, e0, e1);
+        case 32: return launch_h<FP8, 32, 2, 8>(a, s, e0, e1);
+        case 64: return launch_h<FP8, 64, 4, 8>(a, s, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -295,7 +341,11 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width) {
     LogitsPlan p;
     p.m_tiles = num_heads > 16 ? num_heads / 16 : 1;
     p.rows_per_tile = 16 * p.m_tiles / num_heads;
-    p.tiles_per_prog = 4;
+    // 16-column tiles per program: 4 for the few-head decode shapes (a sweep on
+    // MI355X found 1..8 within 4% there), 8 where each program's rows read more
+    // key bytes per column (long single-row and many-head fp8 shapes gained
+    // 3..15%)
+    p.tiles_per_prog = num_heads <= 4 ? 4 : 8;
     return p;
 }
 

@@ -89,6 +89,43 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
     return v;
 }
 
+// DPP (data-parallel primitive) controls, GFX9 encoding
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive scan across the wave with DPP moves (no LDS traffic): row_shr 1, 2,
+// 4, 8 scan each 16-lane row, row_bcast:15 / row_bcast:31 carry row totals into
+// the following rows.  Lanes without a source take `identity`.  All 64 lanes
+// must be active.
+template <class Op>
+__device__ __forceinline__ int wave_scan_dpp(int v, int identity, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr1, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr2, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr4, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr8, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast15, 0xA, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast31, 0xC, 0xF, false));
+    return v;
+}
+
+struct OpAdd {
+    __device__ __forceinline__ int operator()(int a, int b) const { return a + b; }
+};
+struct OpMaxU {
+    __device__ __forceinline__ int operator()(int a, int b) const {
+        return (int)max((uint32_t)a, (uint32_t)b);
+    }
+};
+
+// inclusive prefix sum across the (fully active) wave
+__device__ __forceinline__ int wave_incl_sum(int v) { return wave_scan_dpp(v, 0, OpAdd()); }
+
+// wave-uniform sum / unsigned max (result read from the last lane)
+__device__ __forceinline__ int wave_total_sum(int v) { return readlane(wave_incl_sum(v), 63); }
+__device__ __forceinline__ uint32_t wave_total_umax(uint32_t v) {
+    return (uint32_t)readlane(wave_scan_dpp((int)v, 0, OpMaxU()), 63);
+}
+
 // f32 bits -> u32 whose unsigned order is the float order; -0 is folded onto +0
 // so that the two zeros compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {
