@@ -16,7 +16,7 @@
  * (same page).  Key column c of request b lives in pool block
  * block_table[b, c / B] at slot c % B (same page, block-flat commit; sglang
  * PR #48649 test body).  Columns past a row's visible count are -inf (ROCm/aiter
- * PR #4221 test gate "exact -inf mask").
+ * PR #4221, test gate: the -inf mask is compared exactly).
  *
  * qsa_topk then selects, per row, the k columns of [0, ctx[r]) with the largest
  * logits (vLLM PR #62589, "Details": top-k reads only [0, visible); sglang
@@ -156,21 +156,42 @@ QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const v
  *
  * Device precondition: no NaN inside [0, n_r) (a NaN ranks by its bit pattern:
  * above +inf when its sign is clear, below -inf when set).
+ *
+ *   workspace  device scratch owned by the caller, or NULL.  With NULL every
+ *              row is selected by one workgroup.  Otherwise it must hold at
+ *              least qsa_topk_workspace_bytes(num_rows, width, k) bytes (else
+ *              QSA_E_INVALID) at a 16-byte aligned address (else QSA_E_ALIGN).
+ *              When that size is non-zero (at most 128 rows, width > 4096), each
+ *              row is shared by several workgroups in two kernels that pass
+ *              counts and candidates through the workspace.  Its contents need
+ *              no initialisation and are not kept between calls; calls that
+ *              share a workspace must be ordered (same stream).  The selection
+ *              does not depend on which path runs.
+ *
  * Compiled set (else QSA_E_UNSUPPORTED): 1 <= k <= 2048; width <= 69632.
  * Alignment (else QSA_E_ALIGN): logits 16-byte aligned, logits_stride % 4 == 0.
  */
 QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
-                    int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out, void *stream);
+                            int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out,
+                            void *workspace, int64_t workspace_bytes, void *stream);
 
-/* qsa_topk with the kernel timed by dispatch-recorded events (as
- * qsa_paged_logits_timed). */
+/* Bytes of workspace qsa_topk uses for this shape; 0 when every row is selected
+ * by one workgroup whatever the workspace.  Host-only, no HIP call; k does not
+ * change the size in this build. */
+QSA_API int64_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t width, int32_t k);
+
+/* qsa_topk with its kernels timed by dispatch-recorded events (as
+ * qsa_paged_logits_timed): start_event at the start of the first kernel,
+ * stop_event at the end of the last. */
 QSA_API qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
                                   int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out,
-                                  void *stream, void *start_event, void *stop_event);
+                                  void *workspace, int64_t workspace_bytes, void *stream,
+                                  void *start_event, void *stop_event);
 
 /* Validation of qsa_topk's host-visible arguments only: no HIP call, no launch. */
 QSA_API qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
-                          int32_t num_rows, int32_t width, int32_t k, const int32_t *idx_out);
+                                  int32_t num_rows, int32_t width, int32_t k, const int32_t *idx_out,
+                                  const void *workspace, int64_t workspace_bytes);
 
 /* Message for the calling thread's last non-OK status ("" if none). Owned by the
  * library; valid until the thread's next call. */

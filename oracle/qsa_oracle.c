@@ -18,8 +18,9 @@
  *  - ROCm/aiter PR #4221, "Motivation" and "Technical details": fp8 e4m3 q and
  *    keys, per-key f32 scale, f32 weights w[row, head], output f32; the
  *    block-flat co-packed block (KVB key rows, then KVB f32 scales) and the
- *    block-table gather kv_indices[b, col // KVB], slot col % KVB (commit
- *    "extend fp8_paged_mqa_logits ... KVBlockSize>=1"); exact -inf mask gate.
+ *    block-table gather kv_indices[b, col // KVB], slot col % KVB (the commit
+ *    that extends the fp8 paged kernel to any block size); the -inf mask is
+ *    compared exactly by its test gate.
  *  - vLLM PR #62589, "Overview"/"Details": columns past a row's visible count
  *    are masked; "Validation": top-k reads only [0, visible), compared as sets.
  *

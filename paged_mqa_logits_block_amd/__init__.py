@@ -25,7 +25,8 @@ BF16, FP8_E4M3FN = 0, 1
 KV_PAGED, KV_COPACKED = 0, 1
 
 EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
-            "qsa_topk_timed", "qsa_topk_check", "qsa_last_error", "qsa_version")
+            "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_last_error",
+            "qsa_version")
 
 
 class QsaError(RuntimeError):
@@ -64,12 +65,14 @@ def _load():
     lib.qsa_paged_logits_timed.restype = ctypes.c_int
     lib.qsa_paged_logits_check.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp]
     lib.qsa_paged_logits_check.restype = ctypes.c_int
-    lib.qsa_topk.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp]
+    lib.qsa_topk.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, i64, vp]
     lib.qsa_topk.restype = ctypes.c_int
-    lib.qsa_topk_timed.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, vp, vp]
+    lib.qsa_topk_timed.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, i64, vp, vp, vp]
     lib.qsa_topk_timed.restype = ctypes.c_int
-    lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32, i32, i32, i32p]
+    lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, i64]
     lib.qsa_topk_check.restype = ctypes.c_int
+    lib.qsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.qsa_topk_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_last_error.argtypes = []
     lib.qsa_last_error.restype = ctypes.c_char_p
     lib.qsa_version.argtypes = []
@@ -171,8 +174,33 @@ def paged_logits(q, kcache, block_table, ctx_lens, row_to_req, *, width: int, bl
     return out
 
 
-def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, stream=None, events=None):
-    """``qsa_topk``: int32 ``[R, k]`` selected columns, ascending, -1 padded."""
+def topk_workspace_bytes(num_rows: int, width: int, k: int) -> int:
+    """``qsa_topk_workspace_bytes``: scratch bytes the split selection uses (0: none)."""
+    return int(lib.qsa_topk_workspace_bytes(int(num_rows), int(width), int(k)))
+
+
+def _workspace(workspace, R: int, width: int, k: int, device):
+    """(tensor or None, pointer, bytes) for qsa_topk's workspace argument:
+    "auto" allocates what the shape uses (nothing when it uses none), None
+    passes NULL (one workgroup per row), a uint8 device tensor is passed as is."""
+    import torch
+    if workspace is None:
+        return None, None, 0
+    if isinstance(workspace, str):
+        _require(workspace == "auto", 'workspace must be "auto", None or a device tensor')
+        nbytes = topk_workspace_bytes(R, width, k)
+        if nbytes == 0:
+            return None, None, 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    return workspace, workspace.data_ptr(), int(workspace.numel() * workspace.element_size())
+
+
+def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, workspace="auto",
+         stream=None, events=None):
+    """``qsa_topk``: int32 ``[R, k]`` selected columns, ascending, -1 padded.
+    ``workspace``: "auto" (allocate the scratch the shape uses), None (NULL:
+    one workgroup per row) or a uint8 device tensor."""
     import torch
     _require(logits.is_cuda and ctx_lens.is_cuda, "logits and ctx_lens must be device tensors")
     _require(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
@@ -185,7 +213,9 @@ def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, str
     _require(out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (R, k),
              "out must be contiguous int32 [R, k]")
     stride = int(logits.stride(0)) if R > 0 else width
-    args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), _stream(stream))
+    ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device)
+    args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), ws_ptr, ws_bytes,
+            _stream(stream))
     if events is None:
         st = lib.qsa_topk(*args)
     else:
@@ -201,9 +231,11 @@ def paged_logits_check(q_ptr, w_ptr, kcache_ptr, kscale_ptr, bt_ptr, ctx_ptr, r2
                                       out_ptr, ctypes.byref(shape))
 
 
-def topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr) -> int:
+def topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr, workspace_ptr=None,
+               workspace_bytes=0) -> int:
     """Host-side validation only (``qsa_topk_check``); pointers are ints."""
-    return lib.qsa_topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr)
+    return lib.qsa_topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr, workspace_ptr,
+                              workspace_bytes)
 
 
 class PreparedLogits:
@@ -237,15 +269,20 @@ class PreparedLogits:
 
 
 class PreparedTopk:
-    """A validated ``qsa_topk`` call on fixed tensors (see PreparedLogits)."""
+    """A validated ``qsa_topk`` call on fixed tensors (see PreparedLogits); the
+    workspace ("auto": allocated once here) is part of the prepared call."""
 
-    def __init__(self, logits, ctx_lens, k: int, out, *, width: Optional[int] = None, stream=None):
+    def __init__(self, logits, ctx_lens, k: int, out, *, width: Optional[int] = None, workspace="auto",
+                 stream=None):
         R = int(logits.shape[0])
         width = int(logits.shape[1]) if width is None else int(width)
         stride = int(logits.stride(0)) if R > 0 else width
-        self._keep = (logits, ctx_lens, out)
-        self._args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), _stream(stream))
-        _raise_on(lib.qsa_topk_check(*self._args[:7]))
+        ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device)
+        self._keep = (logits, ctx_lens, out, ws)
+        self.workspace = ws
+        self._args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), ws_ptr, ws_bytes,
+                      _stream(stream))
+        _raise_on(lib.qsa_topk_check(*self._args[:9]))
         self.out = out
 
     def __call__(self, events=None):

@@ -78,7 +78,8 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
 }
 
 qsa_status check_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int32_t num_rows,
-                      int32_t width, int32_t k, const int32_t *idx_out) {
+                      int32_t width, int32_t k, const int32_t *idx_out, const void *workspace,
+                      int64_t workspace_bytes) {
     if (num_rows < 0) return fail(QSA_E_INVALID, "num_rows = %d < 0", num_rows);
     if (width < 0) return fail(QSA_E_INVALID, "width = %d < 0", width);
     if (k < 1) return fail(QSA_E_INVALID, "k = %d < 1", k);
@@ -91,6 +92,12 @@ qsa_status check_topk(const float *logits, int64_t stride, const int32_t *ctx_le
     if ((int64_t)num_rows * stride > kMaxBytes / 4) return fail(QSA_E_RANGE, "num_rows * logits_stride too large");
     if (num_rows > 0 && !aligned16(logits)) return fail(QSA_E_ALIGN, "logits must be 16-byte aligned");
     if (num_rows > 0 && stride % 4 != 0) return fail(QSA_E_ALIGN, "logits_stride must be a multiple of 4");
+    if (workspace) {
+        const int64_t need = qsa::topk_workspace_bytes(num_rows, width);
+        if (workspace_bytes < need)
+            return fail(QSA_E_INVALID, "workspace_bytes = %lld < %lld", (long long)workspace_bytes, (long long)need);
+        if (need > 0 && !aligned16(workspace)) return fail(QSA_E_ALIGN, "workspace must be 16-byte aligned");
+    }
     return ok();
 }
 
@@ -157,23 +164,52 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     return ok();
 }
 
+int64_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t width, int32_t k) {
+    (void)k;
+    if (num_rows < 0 || width < 0) return 0;
+    return qsa::topk_workspace_bytes(num_rows, width);
+}
+
 qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
-                          int32_t width, int32_t k, const int32_t *idx_out) {
-    return check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out);
+                          int32_t width, int32_t k, const int32_t *idx_out, const void *workspace,
+                          int64_t workspace_bytes) {
+    return check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, workspace, workspace_bytes);
 }
 
 qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
-                    int32_t width, int32_t k, int32_t *idx_out, void *stream) {
-    return qsa_topk_timed(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, stream, nullptr, nullptr);
+                    int32_t width, int32_t k, int32_t *idx_out, void *workspace, int64_t workspace_bytes,
+                    void *stream) {
+    return qsa_topk_timed(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, workspace,
+                          workspace_bytes, stream, nullptr, nullptr);
 }
 
 qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
-                          int32_t width, int32_t k, int32_t *idx_out, void *stream, void *start_event,
-                          void *stop_event) {
-    qsa_status st = check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out);
+                          int32_t width, int32_t k, int32_t *idx_out, void *workspace, int64_t workspace_bytes,
+                          void *stream, void *start_event, void *stop_event) {
+    qsa_status st = check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, workspace,
+                               workspace_bytes);
     if (st != QSA_OK) return st;
     if (num_rows == 0) return ok();
-    qsa::TopkArgs a = {logits, logits_stride, ctx_lens, num_rows, width, k, idx_out};
+    qsa::TopkArgs a = {};
+    a.logits = logits;
+    a.stride = logits_stride;
+    a.ctx_lens = ctx_lens;
+    a.num_rows = num_rows;
+    a.width = width;
+    a.k = k;
+    a.idx_out = idx_out;
+    a.slices = 1;
+    a.slice_len = width;
+    if (workspace) {
+        const qsa::TopkPlan p = qsa::plan_topk(num_rows, width);
+        if (p.slices > 1) {
+            a.workspace = static_cast<uint8_t *>(workspace);
+            a.slices = p.slices;
+            a.slice_len = p.slice_len;
+            a.groups = p.groups;
+            a.cand_shift = p.cand_shift;
+        }
+    }
     hipError_t e = qsa::launch_topk(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
                                     static_cast<hipEvent_t>(stop_event));
     if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -57,9 +57,25 @@ struct TopkArgs {
     int32_t width;
     int32_t k;
     int32_t *idx_out;
+    uint8_t *workspace;  // split selection only
+    int32_t slices;      // workgroups per row (1: one workgroup per row)
+    int32_t slice_len;   // columns per slice, a multiple of 4
+    int32_t groups;      // consecutive float4 per thread covering a slice
+    int32_t cand_shift;  // log2 of the member slots per slice
 };
 
-int topk_groups_for_width(int width);  // float4 groups per thread, 0 if too wide
+// How a top-k call is spread: one workgroup per row, or `slices` workgroups
+// per row (few rows) passing counts and members through a workspace.
+struct TopkPlan {
+    int slices;
+    int slice_len;
+    int groups;
+    int cand_shift;
+};
+
+int topk_groups_for_width(int width);  // 1 if the width is supported, else 0
+TopkPlan plan_topk(int num_rows, int width);
+int64_t topk_workspace_bytes(int num_rows, int width);  // 0: no workspace used
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace qsa

@@ -3,7 +3,7 @@
 // Selects, per row, the k columns of [0, n) with the largest logits, ties to
 // the lower column (+0 and -0 equal), and writes them in ascending column order
 // followed by -1 padding.  Rows with n <= k keep all of [0, n) (sglang
-// PR #48649, Accuracy Tests: "decode skips rows that fit topk"); nothing past n
+// PR #48649, Accuracy Tests: rows that fit in k need no selection); nothing past n
 // is used (vLLM PR #62589, Details and Validation).
 //
 // One workgroup of 1024 threads (16 waves) per row.  The selection is reduced to
@@ -64,6 +64,12 @@ struct Shared {
     int ncand;
     int tie_col;
     uint32_t thr_key;
+    // split selection (resolve kernel)
+    int split_above;   // columns of the row above the window
+    int split_before;  // columns kept before this slice, known before the resolve
+    int split_over;    // a slice recorded more members than it has slots
+    int split_n;       // window members of the row
+    int kept_before;   // kept crossing-bucket members before this slice
 };
 
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -75,14 +81,16 @@ __device__ __forceinline__ f32x4 load4(const float *src, int i) {
     return *reinterpret_cast<const f32x4 *>(src + 4 * i);
 }
 
-__device__ __forceinline__ void clear_hist(Shared &sh) {
+template <class Sh>
+__device__ __forceinline__ void clear_hist(Sh &sh) {
     for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0;
 }
 
 // Exclusive scan of hist in bin order; finds the bin where the running count
 // first reaches `need` (1 <= need <= total).  Result lands in sh.cross_*.
 // All threads; ends with a barrier.
-__device__ __forceinline__ void find_crossing(Shared &sh, int need) {
+template <class Sh>
+__device__ __forceinline__ void find_crossing(Sh &sh, int need) {
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int h0 = (int)sh.hist[2 * t], h1 = (int)sh.hist[2 * t + 1];
@@ -412,7 +420,8 @@ struct RowRange {
     bool all_finite;
 };
 
-__device__ __forceinline__ RowRange row_range(Shared &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite) {
+template <class Sh>
+__device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite) {
     const int w = threadIdx.x >> 6;
     kmax = wave_total_umax(kmax);
     const uint32_t nkmin = wave_total_umax(~kmin);
@@ -447,24 +456,15 @@ __device__ __forceinline__ void track(float x, bool valid, uint32_t &kmax, uint3
     nf |= (valid && !fin) ? 1u : 0u;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-    __shared__ Shared sh;
-    const int row = blockIdx.x;
+// The whole selection of one row with n > k columns, by one workgroup.  STAGE:
+// rows of up to kStage columns are staged in LDS; without it (a lighter body
+// for a rare path) every row is re-read from memory on each pass.
+template <bool STAGE = true>
+__device__ __forceinline__ void select_full_row(Shared &sh, const float *src, int n, int k, int32_t *out) {
     const int t = threadIdx.x;
-    const int n = min(max(a.ctx_lens[row], 0), a.width);
-    const int k = a.k;
-    int32_t *out = a.idx_out + (int64_t)row * k;
-
-    if (n <= k) {  // the whole visible range is the selection
-        for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
-        return;
-    }
-
-    const float *src = a.logits + (int64_t)row * a.stride;
     const int n4 = (n + 3) >> 2;
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nonfinite = 0u;
-
-    if (n <= kStage) {
+    if (STAGE && n <= kStage) {
         // ---- 1. stage the row: all loads in flight, then keys to LDS ------
         f32x4 x[kStageGroups];
 #pragma unroll
@@ -531,13 +531,537 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
 }
 
+// ---- one workgroup per row --------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
+    __shared__ Shared sh;
+    const int row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int n = min(max(a.ctx_lens[row], 0), a.width);
+    const int k = a.k;
+    int32_t *out = a.idx_out + (int64_t)row * k;
+    if (n <= k) {  // the whole visible range is the selection
+        for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    select_full_row(sh, a.logits + (int64_t)row * a.stride, n, k, out);
+}
+
+// ---- split selection: several workgroups per row ----------------------------
+//
+// With few rows (decode), one workgroup per row leaves most CUs idle and runs
+// every pass over its row on one CU.  The row is cut into `slices` contiguous
+// slices, one workgroup each; thread t of a slice owns G consecutive float4
+// (columns lo + 4Gt ..), so that column order is thread order.  Two kernels:
+//
+//  window:  every workgroup of a row draws the same sample of the row (128 runs
+//           of 16 columns spread evenly; the whole row when shorter than 2048),
+//           buckets it linearly between its finite min and max, and takes the
+//           buckets holding the sample ranks k*m/n -/+ (4 sigma + 8) of a
+//           binomial count: their edges give thresholds a > b.  Columns >= a
+//           are "above", columns in [b, a) are the window's members.  It counts
+//           its slice's columns above, and records each member (key, column,
+//           member bucket) plus the slice's histogram over kMBins member
+//           buckets, a map linear over the window that every workgroup of the
+//           row shares.
+//  resolve: every workgroup of the row loads the row's counts, histograms and
+//           members and its own slice in one round of loads, finds the member
+//           bucket of the (k - above)-th largest, takes (T, Ct) among that
+//           bucket's members exactly, and writes the kept columns of its slice
+//           at the offset counted from the earlier slices (above + members in
+//           higher buckets + kept members of the crossing bucket).
+//
+// Every workgroup of a row takes the same decisions from the same data, so no
+// workgroup waits for another.  A window that misses the k-th value, or a slice
+// with more members than slots, sends the row down the one-workgroup selection
+// (in the resolve kernel's first slice): the sample decides speed, never the
+// result.  Loads are unconditional at clamped in-row addresses, so a wait for
+// one load never waits for later ones, and the tests are branch-free.
+
+constexpr int kSample = 2048;         // sampled columns per row
+constexpr int kSampleRuns = kSample / 16;
+constexpr int kMBins = 256;           // member buckets
+constexpr int kSliceGroups = 8;       // float4 per thread at most: slices <= 32768 columns
+constexpr int kSlotLoads = 8;         // member slots a resolve thread loads
+constexpr int kHistLoads = 5;         // histogram words a resolve thread loads (17 slices)
+constexpr int kSplitCUs = 256;        // workgroups that fill the chip once
+constexpr int kSplitMaxRows = kSplitCUs / 2;
+
+struct WindowShared {
+    alignas(16) uint32_t hist[kBins];
+    uint32_t mhist[kMBins];
+    uint32_t red_max[kWaves];
+    uint32_t red_min[kWaves];
+    int u_top;
+    int u_bot;
+    int nmem;
+    int nabove;
+};
+
+// Buckets linear in the value, bucket 1 holding vmax and above, bucket
+// top + 1 holding vmax - top/scale and below (infinities clamp to the ends, NaN
+// goes to bucket 1).  Monotone non-increasing in the value.
+struct RangeBucketer {
+    float vmax, scale, top;
+    __device__ __forceinline__ int operator()(float v) const {
+        return 1 + (int)fminf(fmaxf((vmax - v) * scale, 0.0f), top);
+    }
+};
+
+// Range map over [key_value(kmin), key_value(kmax)] with nb buckets (1 .. nb-2);
+// a degenerate range maps everything to bucket 1.
+__device__ __forceinline__ RangeBucketer make_range(float vmax, float vmin, int nb) {
+    const float span = vmax - vmin;
+    const bool usable = span > 0.0f && __builtin_isfinite(span);
+    return RangeBucketer{vmax, usable ? (float)(nb - 3) / span : 0.0f, (float)(nb - 3)};
+}
+
+// unsigned max over the kWaves per-wave partials (one LDS read per wave)
+__device__ __forceinline__ uint32_t partials_umax(const uint32_t *red) {
+    const int l = lane_id();
+    return wave_total_umax(l < kWaves ? red[l] : 0u);
+}
+
+// Bin of hist (64 * 4 * Q bins, in order) where the running count first
+// reaches `need` (1 <= need <= total), and the count before that bin.  One full
+// wave: 4Q bins per lane, then the owning lane's bins one per lane.
+template <int Q>
+__device__ __forceinline__ void wave_crossing(const uint32_t *hist, int need, int &bin, int &before) {
+    constexpr int P = 4 * Q;  // bins per lane
+    const int l = lane_id();
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist) + Q * l;
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        const uint4 v = h4[i];
+        s += (int)(v.x + v.y + v.z + v.w);
+    }
+    const int incl = wave_incl_sum(s);
+    const uint64_t mo = ballot(incl >= need);  // never empty for need <= total
+    const int owner = mo ? __builtin_ctzll(mo) : 63;
+    const int base = readlane(incl - s, owner);
+    const int c = l < P ? (int)hist[P * owner + l] : 0;
+    const int ci = wave_incl_sum(c);
+    const uint64_t ms = ballot(base + ci >= need);
+    const int sub = ms ? min(__builtin_ctzll(ms), P - 1) : P - 1;
+    bin = P * owner + sub;
+    before = base + readlane(ci - c, sub);
+}
+
+struct SplitWorkspace {
+    int2 *meta;      // [rows * slices]: (columns above the window, window members)
+    uint32_t *hist;  // [rows * slices][kMBins]: members per member bucket
+    uint2 *slot;     // [rows * slices][cand_cap]: (key, column | member bucket << 17)
+};
+
+__host__ __device__ __forceinline__ int64_t split_meta_bytes(int rows, int slices) {
+    return ((int64_t)rows * slices * 8 + 255) & ~(int64_t)255;
+}
+
+__device__ __forceinline__ SplitWorkspace split_ws(const TopkArgs &a) {
+    const int64_t rs = (int64_t)a.num_rows * a.slices;
+    SplitWorkspace w;
+    w.meta = reinterpret_cast<int2 *>(a.workspace);
+    w.hist = reinterpret_cast<uint32_t *>(a.workspace + split_meta_bytes(a.num_rows, a.slices));
+    w.slot = reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(w.hist) + rs * kMBins * 4);
+    return w;
+}
+
+// value of register slot b (float4 b >> 2, element b & 3) of x: static selects
+template <int G>
+__device__ __forceinline__ float pick(const f32x4 (&x)[G], int b) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4 * G; ++q) v = (q == b) ? x[q >> 2][q & 3] : v;
+    return v;
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a) {
+    __shared__ WindowShared sh;
+    const int row = blockIdx.x / a.slices;
+    const int s = blockIdx.x - row * a.slices;
+    const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int n = min(max(a.ctx_lens[row], 0), a.width);
+    const int k = a.k;
+    const int lo = s * a.slice_len;
+    if (n <= k || lo >= n) return;
+    const int hi = min(n, lo + a.slice_len);
+    const int n4 = (n + 3) >> 2;
+    const float *src = a.logits + (int64_t)row * a.stride;
+
+    // the sample first (it is used first), then this thread's float4 of the slice
+    const int m = n >= kSample ? kSample : n;
+    const int ts = t & (kSample / 4 - 1);
+    int sc;
+    if (n >= kSample) {
+        const int run = ts >> 2;
+        const int center = (int)(((int64_t)(2 * run + 1) * n) / (2 * kSampleRuns));
+        sc = (min(max(center - 8, 0), n - 16) & ~3) + 4 * (ts & 3);
+    } else {
+        sc = 4 * ts;
+    }
+    const f32x4 y = load4(src, min(sc >> 2, n4 - 1));
+    if (t >= kSample / 4) sc = n;  // one sample per column: the first 512 threads
+    const int c0 = lo + 4 * G * t;   // this thread's first column
+    f32x4 x[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = load4(src, min((c0 >> 2) + j, n4 - 1));
+
+    clear_hist(sh);
+    if (t < kMBins) sh.mhist[t] = 0u;
+    if (t == 0) {
+        sh.nmem = 0;
+        sh.nabove = 0;
+    }
+    // finite range of the sample
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nonfinite = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) track(y[e], sc + e < n, kmax, kmin, nonfinite);
+    kmax = wave_total_umax(kmax);
+    const uint32_t nkmin = wave_total_umax(~kmin);
+    if (l == 0) {
+        sh.red_max[w] = kmax;
+        sh.red_min[w] = nkmin;
+    }
+    __syncthreads();
+    const uint32_t gmax = partials_umax(sh.red_max);
+    const uint32_t gmin = ~partials_umax(sh.red_min);
+    const bool have = gmax != 0u;  // some finite sample
+    const float smax = key_value(gmax), smin = key_value(gmin);
+    const RangeBucketer sb = have ? make_range(smax, smin, kBins) : RangeBucketer{0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (sc + e < n) atomicAdd(&sh.hist[sb(y[e])], 1u);
+    __syncthreads();
+    if (w == 0) {  // sample buckets of the ranks around the k-th largest
+        const float p = (float)k / (float)n;
+        const float mean = p * (float)m;
+        const float dev = 4.0f * sqrtf((float)m * p * (1.0f - p)) + 8.0f;
+        const int top_rank = (int)floorf(mean - dev);
+        const int bot_rank = (int)ceilf(mean + dev);
+        int u_top = 0, u_bot = kBins - 1, before;
+        if (top_rank >= 1) wave_crossing<kBins / 256>(sh.hist, top_rank, u_top, before);
+        if (bot_rank <= m) wave_crossing<kBins / 256>(sh.hist, bot_rank, u_bot, before);
+        if (l == 0) {
+            sh.u_top = u_top;
+            sh.u_bot = u_bot;
+        }
+    }
+    __syncthreads();
+    // thresholds at the bucket edges (any values give the right result)
+    const int u_top = sh.u_top, u_bot = sh.u_bot;
+    const bool sampled = sb.scale > 0.0f;
+    const float a_val = (u_top <= 1 || !sampled) ? __builtin_inff() : sb.vmax - (float)(u_top - 1) / sb.scale;
+    const float b_val = (u_bot >= kBins - 2 || !sampled) ? -__builtin_inff() : sb.vmax - (float)u_bot / sb.scale;
+    // member buckets: linear over the window, or over the sampled range where
+    // the window is open
+    const float mtop = __builtin_isfinite(a_val) ? a_val : smax;
+    const float mlow = __builtin_isfinite(b_val) ? b_val : smin;
+    const RangeBucketer mbk = have ? make_range(mtop, mlow, kMBins) : RangeBucketer{0.0f, 0.0f, 0.0f};
+
+    // the slice: columns above, member bits (bit 4j + e)
+    int above = 0;
+    uint32_t mbits = 0u;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = x[j][e];
+            const bool valid = c0 + 4 * j + e < hi;
+            const bool ge_a = v >= a_val;
+            above += __popcll(ballot(valid & ge_a));
+            mbits |= (uint32_t)(valid & (v >= b_val) & !ge_a) << (4 * j + e);
+        }
+    }
+    const int nmem = __popc(mbits);
+    const int mincl = wave_incl_sum(nmem);
+    int wbase = 0;
+    if (l == 63 && mincl > 0) wbase = atomicAdd(&sh.nmem, mincl);
+    wbase = readlane(wbase, 63);
+    if (l == 0 && above) atomicAdd(&sh.nabove, above);
+    const SplitWorkspace ws = split_ws(a);
+    const int64_t rs = (int64_t)row * a.slices + s;
+    uint2 *slot = ws.slot + (rs << a.cand_shift);
+    const int cap = 1 << a.cand_shift;
+    int at = wbase + mincl - nmem;
+    while (mbits) {  // ~ a few percent of the columns: per-lane loop
+        const int b = __builtin_ctz(mbits);
+        mbits &= mbits - 1u;
+        const float v = pick<G>(x, b);
+        const int mb = mbk(v);
+        if (at < cap) slot[at] = make_uint2(order_key(v), (uint32_t)(c0 + b) | ((uint32_t)mb << 17));
+        atomicAdd(&sh.mhist[mb], 1u);
+        ++at;
+    }
+    __syncthreads();
+    if (t < kMBins) ws.hist[rs * kMBins + t] = sh.mhist[t];
+    if (t == 0) ws.meta[rs] = make_int2(sh.nabove, sh.nmem);
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
+    __shared__ Shared sh;
+    const int row = blockIdx.x / a.slices;
+    const int s = blockIdx.x - row * a.slices;
+    const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int n = min(max(a.ctx_lens[row], 0), a.width);
+    const int k = a.k;
+    int32_t *out = a.idx_out + (int64_t)row * k;
+    const float *src = a.logits + (int64_t)row * a.stride;
+    if (n <= k) {
+        if (s == 0)
+            for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    const int lo = s * a.slice_len;
+    if (lo >= n) return;
+    const int hi = min(n, lo + a.slice_len);
+    const int ns = (n + a.slice_len - 1) / a.slice_len;  // slices of this row (<= 64)
+    const int n4 = (n + 3) >> 2;
+
+    // one round of loads: this thread's slice float4, the row's counts,
+    // histograms and member slots (unconditional, clamped)
+    const int c0 = lo + 4 * G * t;
+    f32x4 x[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = load4(src, min((c0 >> 2) + j, n4 - 1));
+    const SplitWorkspace ws = split_ws(a);
+    const int64_t rs0 = (int64_t)row * a.slices;
+    const int2 mt = ws.meta[rs0 + min(l, ns - 1)];
+    const int nh = ns * kMBins;
+    uint32_t hv[kHistLoads];
+#pragma unroll
+    for (int u = 0; u < kHistLoads; ++u) hv[u] = ws.hist[rs0 * kMBins + min(t + kThreads * u, nh - 1)];
+    const int nslots = ns << a.cand_shift;
+    uint2 sv[kSlotLoads];
+#pragma unroll
+    for (int u = 0; u < kSlotLoads; ++u) sv[u] = ws.slot[(rs0 << a.cand_shift) + min(t + kThreads * u, nslots - 1)];
+
+    // row totals; histograms into LDS (per slice, and summed over slices)
+    uint32_t *hs = sh.keys;  // [ns][kMBins]
+    uint32_t *tot = sh.hist; // [kMBins]
+    if (t < kMBins) tot[t] = 0u;
+    if (t == 0) sh.ncand = 0;
+    if (w == 0) {
+        const int ab = l < ns ? mt.x : 0;
+        const int nm = l < ns ? mt.y : 0;
+        const int ai = wave_incl_sum(ab);
+        const uint64_t over = ballot(nm > (1 << a.cand_shift));
+        if (l < ns) sh.grp[l] = nm;  // members of slice l
+        if (l == s) sh.split_before = ai - ab;
+        if (l == 63) {
+            sh.split_above = ai;
+            sh.split_over = over != 0;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kHistLoads; ++u) {
+        const int f = t + kThreads * u;
+        if (f < nh) {
+            hs[f] = hv[u];
+            if (hv[u]) atomicAdd(&tot[f & (kMBins - 1)], hv[u]);
+        }
+    }
+    __syncthreads();
+    const int need = k - sh.split_above;
+    if (w == 0) {  // crossing bucket; members above it in earlier slices
+        int nall = 0;
+        {
+            const uint4 v = reinterpret_cast<const uint4 *>(tot)[l];
+            nall = wave_total_sum((int)(v.x + v.y + v.z + v.w));
+        }
+        int bin = 0, before = 0;
+        if (need >= 1 && need <= nall) wave_crossing<1>(tot, need, bin, before);
+        int below = 0;  // members of slices < s in buckets < bin
+        for (int j = 0; j < s; ++j) {
+            const uint4 v = reinterpret_cast<const uint4 *>(hs + j * kMBins)[l];
+            const int b0 = 4 * l;
+            below += (b0 < bin ? (int)v.x : 0) + (b0 + 1 < bin ? (int)v.y : 0) +
+                     (b0 + 2 < bin ? (int)v.z : 0) + (b0 + 3 < bin ? (int)v.w : 0);
+        }
+        below = wave_total_sum(below);
+        if (l == 0) {
+            sh.split_n = nall;
+            sh.cross_bin = bin;
+            sh.cross_above = before;
+            sh.cross_cnt = (int)tot[bin];
+            sh.split_before += below;
+            sh.kept_before = 0;
+        }
+    }
+    __syncthreads();
+    const int N = sh.split_n;
+    const int cnt = sh.cross_cnt;
+    if (sh.split_over || need < 1 || need > N || cnt > kCand) {
+        if (s == 0) select_full_row<false>(sh, src, n, k, out);
+        return;
+    }
+    const int bstar = sh.cross_bin;
+    const int need2 = need - sh.cross_above;
+
+    // members of the crossing bucket -> (key, column) list
+#pragma unroll
+    for (int u = 0; u < kSlotLoads; ++u) {
+        const int f = t + kThreads * u;
+        const int j = f >> a.cand_shift;
+        const bool hit = f < nslots && (f & ((1 << a.cand_shift) - 1)) < sh.grp[min(j, ns - 1)] &&
+                         (int)(sv[u].y >> 17) == bstar;
+        const uint64_t mk = ballot(hit);
+        if (mk) {
+            const int lead = __builtin_ctzll(mk);
+            int base = 0;
+            if (l == lead) base = atomicAdd(&sh.ncand, __popcll(mk));
+            base = readlane(base, lead);
+            if (hit) {
+                const int at = base + mask_prefix(mk);
+                sh.cand_key[at] = sv[u].x;
+                sh.cand_col[at] = (int)(sv[u].y & 0x1FFFFu);
+            }
+        }
+    }
+    __syncthreads();
+
+    // the k-th pair (T, Ct) inside the crossing bucket
+    uint32_t T;
+    int Ct;
+    if (cnt <= 64) {
+        if (w == 0) {
+            const uint32_t mk = l < cnt ? sh.cand_key[l] : 0u;
+            const int mc = l < cnt ? sh.cand_col[l] : 0x7FFFFFFF;
+            int rank = 0;
+            for (int j = 0; j < cnt; ++j) {
+                const uint32_t kj = (uint32_t)readlane((int)mk, j);
+                const int cj = readlane(mc, j);
+                rank += (kj > mk || (kj == mk && cj < mc)) ? 1 : 0;
+            }
+            if (l < cnt && rank == need2 - 1) {
+                sh.thr_key = mk;
+                sh.tie_col = mc;
+            }
+            // kept members of the crossing bucket in earlier slices
+            const bool kept_early = l < cnt && mc < lo && rank <= need2 - 1;
+            const int kb = __popcll(ballot(kept_early));
+            if (l == 0) sh.kept_before = kb;
+        }
+        __syncthreads();
+        T = sh.thr_key;
+        Ct = sh.tie_col;
+    } else {
+        int need3 = need2, cnt3 = 0;
+        radix_select(sh, [&](auto f) {
+            for (int j = t; j < cnt; j += kThreads) f(sh.cand_key[j]);
+        }, T, need3, cnt3);
+        if (cnt3 > need3) {  // split the keys equal to T: need3-th lowest column
+            uint32_t nc_key;
+            int need4 = need3, cnt4 = 0;
+            radix_select(sh, [&](auto f) {
+                for (int j = t; j < cnt; j += kThreads)
+                    if (sh.cand_key[j] == T) f(~(uint32_t)sh.cand_col[j]);
+            }, nc_key, need4, cnt4);
+            Ct = (int)~nc_key;
+        } else {
+            Ct = 0x7FFFFFFF;
+        }
+        int kb = 0;
+        for (int j = t; j < cnt; j += kThreads) {
+            const uint32_t key = sh.cand_key[j];
+            const int col = sh.cand_col[j];
+            kb += (col < lo && (key > T || (key == T && col <= Ct))) ? 1 : 0;
+        }
+        kb = wave_total_sum(kb);
+        if (l == 0 && kb) atomicAdd(&sh.kept_before, kb);
+    }
+    const float tv = key_value(T);
+
+    // this slice's kept columns: thread order is column order
+    uint32_t sel = 0u;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int col = c0 + 4 * j + e;
+            const float v = x[j][e];
+            sel |= (uint32_t)((col < hi) & ((v > tv) | ((v == tv) & (col <= Ct)))) << (4 * j + e);
+        }
+    const int mine = __popc(sel);
+    const int incl = wave_incl_sum(mine);
+    if (l == 63) sh.wave_tot[w] = incl;
+    __syncthreads();
+    const int wt = l < kWaves ? sh.wave_tot[l] : 0;
+    const int wincl = wave_incl_sum(wt);
+    int p = sh.split_before + sh.kept_before + readlane(wincl - wt, w) + incl - mine;
+    while (sel) {
+        const int b = __builtin_ctz(sel);
+        sel &= sel - 1u;
+        if (p < k) out[p] = c0 + b;
+        ++p;
+    }
+}
+
 }  // namespace
 
 int topk_groups_for_width(int width) { return width <= kMaxWidth ? 1 : 0; }
 
+TopkPlan plan_topk(int num_rows, int width) {
+    TopkPlan p{1, width, 0, 0};
+    if (num_rows <= 0 || num_rows > kSplitMaxRows || width <= 4 * kThreads) return p;
+    const int by_len = (width + 4 * kThreads - 1) / (4 * kThreads);  // slices of >= 4096 columns
+    const int min_sl = (width + 4 * kThreads * kSliceGroups - 1) / (4 * kThreads * kSliceGroups);
+    int sl = kSplitCUs / num_rows;  // one round of workgroups
+    sl = sl < by_len ? sl : by_len;
+    sl = sl > min_sl ? sl : min_sl;
+    if (sl < 2) return p;
+    int len = (width + sl - 1) / sl;
+    len = (len + 3) & ~3;
+    p.slices = (width + len - 1) / len;
+    p.slice_len = len;
+    p.groups = (len + 4 * kThreads - 1) / (4 * kThreads);
+    // member slots per slice: a power of two >= 1/12 of the slice, all of a
+    // row's slots loadable by one resolve workgroup in one round
+    int shift = 8;
+    while ((1 << shift) < len / 12) ++shift;
+    while (shift > 6 && ((int64_t)p.slices << shift) > (int64_t)kSlotLoads * kThreads) --shift;
+    p.cand_shift = shift;
+    return p;
+}
+
+int64_t topk_workspace_bytes(int num_rows, int width) {
+    const TopkPlan p = plan_topk(num_rows, width);
+    if (p.slices < 2) return 0;
+    const int64_t rs = (int64_t)num_rows * p.slices;
+    return split_meta_bytes(num_rows, p.slices) + rs * kMBins * 4 + (rs << p.cand_shift) * 8;
+}
+
+template <int G>
+static void launch_split(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    const unsigned g = (unsigned)a.num_rows * (unsigned)a.slices;
+    hipExtLaunchKernelGGL(topk_window_kernel<G>, dim3(g), dim3(kThreads), 0, s, start, nullptr, 0, a);
+    hipExtLaunchKernelGGL(topk_resolve_kernel<G>, dim3(g), dim3(kThreads), 0, s, nullptr, stop, 0, a);
+}
+
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     if (a.num_rows == 0) return hipSuccess;
-    hipExtLaunchKernelGGL(topk_kernel, dim3((unsigned)a.num_rows), dim3(kThreads), 0, s, start, stop, 0, a);
+    if (a.slices > 1) {
+        switch (a.groups) {
+            case 1: launch_split<1>(a, s, start, stop); break;
+            case 2: launch_split<2>(a, s, start, stop); break;
+            case 3: launch_split<3>(a, s, start, stop); break;
+            case 4: launch_split<4>(a, s, start, stop); break;
+            case 5: launch_split<5>(a, s, start, stop); break;
+            case 6: launch_split<6>(a, s, start, stop); break;
+            case 7: launch_split<7>(a, s, start, stop); break;
+            case 8: launch_split<8>(a, s, start, stop); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        hipExtLaunchKernelGGL(topk_kernel, dim3((unsigned)a.num_rows), dim3(kThreads), 0, s, start, stop, 0, a);
+    }
     return hipGetLastError();
 }
 

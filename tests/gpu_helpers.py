@@ -38,8 +38,13 @@ def gpu_logits(inp, dev=None, out=None, stream=None):
                           layout=dev.layout, out=out, stream=stream)
 
 
-def gpu_topk(logits_t, ctx_t, k, width=None):
-    return qsa().topk(logits_t, ctx_t, k, width=width)
+def gpu_topk(logits_t, ctx_t, k, width=None, workspace="auto"):
+    """qsa_topk; workspace "auto" takes the split selection where the shape has
+    one, None forces one workgroup per row."""
+    return qsa().topk(logits_t, ctx_t, k, width=width, workspace=workspace)
+
+
+TOPK_PATHS = {"split": "auto", "single": None}
 
 
 def bf16_tol(o):

@@ -121,6 +121,30 @@ def test_topk_validation(args, status):
     assert st == status, (st, m.last_error())
 
 
+@pytest.mark.parametrize("rows,width,split", [
+    (36, 29408, True), (64, 65600, True), (64, 32768, True), (128, 8192, True), (15, 69632, True),
+    (8, 3008, False), (36, 4096, False), (129, 29408, False), (16384, 28672, False), (0, 29408, False),
+])
+def test_topk_workspace_size(rows, width, split):
+    """Few long rows use the split selection (a workspace); many rows, or rows
+    of at most 4096 columns, use one workgroup per row (no workspace)."""
+    nbytes = m.topk_workspace_bytes(rows, width, 2048)
+    assert (nbytes > 0) == split, nbytes
+    if split:  # counts, a 256-bucket histogram and <= 8192 member slots of 8 bytes per row
+        assert nbytes <= rows * (17 * 8 + 17 * 1024 + 8192 * 8) + 256
+
+
+def test_topk_workspace_validation():
+    need = m.topk_workspace_bytes(36, 29408, 2048)
+    base = (A, 29408, A, 36, 29408, 2048, A)
+    assert m.topk_check(*base, None, 0) == m.OK                 # NULL: one workgroup per row
+    assert m.topk_check(*base, A, need) == m.OK
+    assert m.topk_check(*base, A, need - 1) == m.E_INVALID
+    assert m.topk_check(*base, A + 8, need) == m.E_ALIGN
+    # a shape that uses no workspace accepts any
+    assert m.topk_check(A, 3008, A, 8, 3008, 256, A, A + 8, 0) == m.OK
+
+
 def test_one_hip_runtime_in_process():
     """The binding must share torch's HIP runtime (streams and allocations are
     torch's); a second copy of libamdhip64 in the process breaks launches."""

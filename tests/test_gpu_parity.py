@@ -13,8 +13,8 @@ import pytest
 
 import oracle
 import qsa_inputs
-from gpu_helpers import (assert_logits_match, assert_topk_banded, assert_topk_exact, gpu_logits,
-                         gpu_topk, topk_tol)
+from gpu_helpers import (TOPK_PATHS, qsa, assert_logits_match, assert_topk_banded, assert_topk_exact,
+                         gpu_logits, gpu_topk, topk_tol)
 from qsa_inputs.device import to_device
 
 pytestmark = pytest.mark.gpu
@@ -214,16 +214,17 @@ def test_empty_inputs():
 # top-k edge cases (identical logits on both sides: exact)
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("path", sorted(TOPK_PATHS))
 @pytest.mark.parametrize("kind", ["normal", "ints", "const", "zeros", "relu"])
 @pytest.mark.parametrize("k", [1, 7, 256, 2048])
-def test_topk_distributions(kind, k):
+def test_topk_distributions(kind, k, path):
     W = 9000
     ctx = [0, 1, k - 1 if k > 1 else 0, k, k + 1, 3000, 8999, 9000, 12000, 4097]
     x = qsa_inputs.make_logits(len(ctx), W, ctx, seed=k * 7 + len(kind), kind=kind, tail="nan")
-    say("topk", kind, k)
+    say("topk", kind, k, path)
     xt = torch.from_numpy(x).cuda()
     ct = torch.tensor(ctx, dtype=torch.int32, device="cuda")
-    gi = gpu_topk(xt, ct, k).cpu().numpy()
+    gi = gpu_topk(xt, ct, k, workspace=TOPK_PATHS[path]).cpu().numpy()
     ctx_np = np.minimum(np.maximum(np.array(ctx), 0), W)
     xo = x.copy()
     for r, c in enumerate(ctx_np):
@@ -232,8 +233,9 @@ def test_topk_distributions(kind, k):
     assert_topk_exact(gi, oi, label=f"{kind}/k{k}")
 
 
+@pytest.mark.parametrize("path", sorted(TOPK_PATHS))
 @pytest.mark.parametrize("W", [69632, 65600, 32768, 4096, 4099])
-def test_topk_widths_and_large_tie_buckets(W):
+def test_topk_widths_and_large_tie_buckets(W, path):
     # const rows put everything in one bucket (larger than the LDS list);
     # ints rows make large tie groups inside the list
     rows = []
@@ -241,13 +243,88 @@ def test_topk_widths_and_large_tie_buckets(W):
         rows.append(qsa_inputs.make_logits(2, W, [W, W - 3], seed=W % 97, kind=kind))
     x = np.concatenate(rows)
     ctx = np.array([W, W - 3] * 3)
-    say("topk width", W)
+    say("topk width", W, path)
     stride = (W + 3) // 4 * 4  # rows padded to a multiple of 4 floats
     xt = torch.full((x.shape[0], stride), float("nan"), dtype=torch.float32, device="cuda")
     xt[:, :W] = torch.from_numpy(x).cuda()
-    gi = gpu_topk(xt[:, :W], torch.from_numpy(ctx.astype(np.int32)).cuda(), 2048, width=W).cpu().numpy()
+    gi = gpu_topk(xt[:, :W], torch.from_numpy(ctx.astype(np.int32)).cuda(), 2048, width=W,
+                  workspace=TOPK_PATHS[path]).cpu().numpy()
     oi = oracle.topk(x, ctx, 2048)
     assert_topk_exact(gi, oi, label=f"W{W}")
+
+
+def _sampled_columns(n):
+    """Columns the window selection samples from a row of n >= 2048 columns:
+    128 runs of 16, centred at (2r+1) n / 256, clamped and aligned to 4."""
+    cols = []
+    for r in range(128):
+        c = ((2 * r + 1) * n) // 256
+        st = min(max(c - 8, 0), n - 16) & ~3
+        cols.extend(range(st, st + 16))
+    return np.unique(np.array(cols))
+
+
+@pytest.mark.parametrize("rows,W,k", [(36, 29408, 2048), (128, 8192, 2048), (64, 65600, 2048),
+                                      (5, 69632, 1), (17, 12000, 900), (2, 5000, 2047),
+                                      (300, 9000, 2048), (260, 40000, 64)])
+def test_topk_rows_shared_or_not(rows, W, k):
+    """Few rows (split selection: each row shared by several workgroups) and
+    many rows (one workgroup per row), ragged ctx, mixed distributions: both
+    paths equal the oracle."""
+    rng = np.random.default_rng(rows * 1000 + k)
+    ctx = rng.integers(0, W + 1, size=rows)
+    ctx[: min(rows, 3)] = [W, k + 1, max(k - 1, 0)][: min(rows, 3)]
+    kinds = ["normal", "relu", "ints", "normal"]
+    x = np.concatenate([qsa_inputs.make_logits(1, W, [int(ctx[r])], seed=r + 31, kind=kinds[r % 4])
+                        for r in range(rows)])
+    say("topk rows", rows, W, k)
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    oi = oracle.topk(x, ctx, k)
+    g = gpu_topk(xt, ct, k).cpu().numpy()
+    assert_topk_exact(g, oi, label=f"rows {rows}")
+    g1 = gpu_topk(xt, ct, k, workspace=None).cpu().numpy()
+    assert_topk_exact(g1, oi, label=f"rows {rows} one workgroup per row")
+
+
+def test_topk_sample_miss_falls_back():
+    """Rows whose sampled columns are far below (or above) the rest: the
+    sample's window misses the k-th value and the row takes the histogram
+    selection; the result is unchanged."""
+    W, k, rows = 20000, 2048, 8
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((rows, W)).astype(np.float32)
+    ctx = np.array([W, W, 15000, 9000, 4500, 2100, W, 12345])
+    for r in range(rows):
+        n = int(min(ctx[r], W))
+        if n >= 2048:
+            sc = _sampled_columns(n)
+            x[r, sc] = -1000.0 + rng.standard_normal(len(sc)).astype(np.float32)
+        if r == 6:  # and one row where the sample sits far above the rest
+            x[r, _sampled_columns(n)] = 1000.0
+    say("topk sample miss")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    gs = gpu_topk(xt, ct, k).cpu().numpy()
+    oi = oracle.topk(x, ctx, k)
+    assert_topk_exact(gs, oi, label="sample miss")
+
+
+def test_topk_workspace_reused_across_calls():
+    """One workspace through several calls (different data and ctx, poisoned
+    beforehand): each result equals the oracle; no state survives a call."""
+    m = qsa()
+    W, k, rows = 30000, 2048, 36
+    nbytes = m.topk_workspace_bytes(rows, W, k)
+    assert nbytes > 0
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    say("topk workspace reuse")
+    for seed in (1, 2, 3):
+        rng = np.random.default_rng(seed)
+        ctx = rng.integers(k - 10, W + 1, size=rows).astype(np.int32)
+        x = qsa_inputs.make_logits(rows, W, ctx, seed=seed, kind="normal")
+        g = m.topk(torch.from_numpy(x).cuda(), torch.from_numpy(ctx).cuda(), k, workspace=ws).cpu().numpy()
+        assert_topk_exact(g, oracle.topk(x, ctx, k), label=f"reuse {seed}")
 
 
 def test_topk_padded_row_stride():

@@ -4,8 +4,8 @@ Each case plants one plausible mistake in a *copy* of the oracle source, builds
 it into a temporary library, and requires at least one pin to fail against it.
 A pin set that lets a mutation through is too weak to trust the oracle with.
 (The pages use the same technique on their kernels: vLLM PR #62589, Validation,
-"moving the visible bound by one column"; ROCm/aiter PR #4221, curated-matrix
-commit, eleven deliberate kernel bugs.)
+shifts the visible bound by one column on purpose; ROCm/aiter PR #4221,
+curated-matrix commit, plants eleven kernel bugs.)
 """
 import os
 
