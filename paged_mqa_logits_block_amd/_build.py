@@ -22,6 +22,9 @@ FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the head reduction reads every accumulator with
+    # VALU ops, which would otherwise each need an AGPR-to-VGPR move first
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden",
 ]
 

@@ -127,7 +127,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     if (s->num_rows == 0 || s->width == 0) return ok();
     const bool fp8 = s->k_dtype == QSA_FP8_E4M3FN;
     const int64_t elt = fp8 ? 1 : 2;
-    qsa::LogitsPlan plan = qsa::plan_logits(fp8 ? 1 : 0, s->num_heads, s->num_rows, s->width);
+    qsa::LogitsPlan plan = qsa::plan_logits(fp8 ? 1 : 0, s->num_heads, s->num_rows, s->num_reqs, s->width);
     qsa::LogitsArgs a = {};
     a.q = q;
     a.w = w;
@@ -157,6 +157,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     a.key_stride = s->head_dim * elt;
     a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout == QSA_KV_COPACKED ? 4 * s->block_size : 0);
     a.scale_offset = (int64_t)s->block_size * a.key_stride;
+    a.iters = plan.iters;
     hipError_t e = qsa::launch_paged_logits(a, plan, static_cast<hipStream_t>(stream),
                                             static_cast<hipEvent_t>(start_event),
                                             static_cast<hipEvent_t>(stop_event));

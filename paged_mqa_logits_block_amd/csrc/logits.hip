@@ -29,6 +29,20 @@ namespace {
 
 constexpr int kD = 128;
 
+// Column -> (block index, slot) walked in steps of one 16-column tile: one
+// division per program instead of a division and a remainder per tile (a
+// runtime divisor costs dozens of scalar instructions).  Needs B >= 16.
+struct ColCursor {
+    int q, r;  // block index and slot of the current column
+    __device__ __forceinline__ ColCursor(int col, int bs) : q(col / bs), r(col - (col / bs) * bs) {}
+    __device__ __forceinline__ void step(int bs) {
+        r += 16;
+        const bool wrap = r >= bs;
+        r = wrap ? r - bs : r;
+        q = wrap ? q + 1 : q;
+    }
+};
+
 template <bool FP8>
 struct Frag;
 
@@ -37,10 +51,10 @@ template <>
 struct Frag<false> {
     static constexpr int kSteps = 4;
     typedef bf16x8 T;
-    // lane's slice of one 16-element row of D for K step s
-    __device__ static T load(const uint8_t *row_bytes, int l, int s) {
-        return *reinterpret_cast<const T *>(row_bytes + s * 64 + (l >> 4) * 16);
-    }
+    // byte offset of lane l's slice inside a 16-element row of D (K step 0)
+    __device__ static int lane_bytes(int l) { return (l >> 4) * 16; }
+    // the slice for K step s at p (p includes the lane's offset)
+    __device__ static T load(const uint8_t *p, int s) { return *reinterpret_cast<const T *>(p + s * 64); }
     __device__ static T zero() {
         T z;
 #pragma unroll
@@ -59,14 +73,10 @@ template <>
 struct Frag<true> {
     static constexpr int kSteps = 1;
     typedef i32x8 T;
-    __device__ static T load(const uint8_t *row_bytes, int l, int s) {
+    __device__ static int lane_bytes(int l) { return (l >> 4) * 32; }
+    __device__ static T load(const uint8_t *p, int s) {
         (void)s;
-        const i32x4 *p = reinterpret_cast<const i32x4 *>(row_bytes + (l >> 4) * 32);
-        i32x4 lo = p[0], hi = p[1];
-        T r;
-        r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-        r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-        return r;
+        return *reinterpret_cast<const T *>(p);  // 32 bytes, 32-byte aligned
     }
     __device__ static T zero() {
         T z;
@@ -126,10 +136,10 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         const int m = 16 * mt + (l & 15);
         const int row = row0 + m / H, h = m % H;
         const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) +
-                              ((int64_t)row * H + h) * F::kRowBytes;
+                              ((int64_t)row * H + h) * F::kRowBytes + F::lane_bytes(l);
 #pragma unroll
         for (int s = 0; s < F::kSteps; ++s)
-            qa[mt][s] = (row < a.num_rows) ? F::load(qrow, l, s) : F::zero();
+            qa[mt][s] = (row < a.num_rows) ? F::load(qrow, s) : F::zero();
     }
 
     // weights of the accumulator slots this lane holds: slot (mt, i) is stacked
@@ -206,26 +216,32 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         float kscale[TPW];
         bool ok[TPW];
         if (any_live) {
-            int blk[TPW];
+            int blk[TPW], slot0[TPW];
+            ColCursor cur(c0, a.block_size);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                blk[t] = req_ok ? bt[min((c0 + 16 * t) / a.block_size, a.max_blocks - 1)] : -1;
+            for (int t = 0; t < TPW; ++t) {
+                blk[t] = req_ok ? bt[min(cur.q, a.max_blocks - 1)] : -1;
+                slot0[t] = cur.r;
+                cur.step(a.block_size);
+            }
+            // per lane: key column l % 16 of the tile, its slice of the row
+            const int lane_key = (l & 15) * (int)a.key_stride + F::lane_bytes(l);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int col0 = c0 + 16 * t;
                 ok[t] = col0 < vis && blk[t] >= 0 && (int64_t)blk[t] < a.num_blocks;
-                const int slot = (col0 % a.block_size) + (l & 15);
-                const int64_t boff = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
-                const uint8_t *kb = a.kcache + boff;
-                const uint8_t *krow = kb + (int64_t)(ok[t] ? slot : (l & 15)) * a.key_stride;
+                // wave-uniform tile base (block 0 when the tile is not scored)
+                const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
+                const int tslot = ok[t] ? slot0[t] : 0;
+                const uint8_t *kt = a.kcache + bbase + (int64_t)tslot * a.key_stride;
 #pragma unroll
-                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(krow, l, s);
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kt + lane_key, s);
                 kscale[t] = 1.0f;
                 if (HAS_SCALE) {
                     if (a.layout == 1)
-                        kscale[t] = *reinterpret_cast<const float *>(kb + a.scale_offset + 4 * (ok[t] ? slot : 0));
+                        kscale[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
                     else
-                        kscale[t] = a.kscale[ok[t] ? (int64_t)blk[t] * a.block_size + slot : 0];
+                        kscale[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
                 }
             }
         } else {
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                 for (int j = 0; j < NR; ++j) {
                     float v = 0.0f;
 #pragma unroll
-                    for (int i = j * H; i < j * H + H; ++i) v += wv[0][i] * fmaxf(acc[0][i], 0.0f);
+                    for (int i = j * H; i < j * H + H; ++i) v += wv[0][i] * relu(acc[0][i]);
                     val[t][j] = v;
                 }
             } else {
@@ -267,37 +283,247 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     // all 4 slots of tile mt belong to tile row (16*mt + 4*g) / H
-                    const int rr = (16 * mt + 4 * g) / H;
+                    // (16*mt / H for H >= 16: known at compile time)
+                    const int rr = H >= 16 ? (16 * mt) / H : (16 * mt + 4 * g) / H;
                     float c = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) c += wv[mt][i] * fmaxf(acc[mt][i], 0.0f);
+                    for (int i = 0; i < 4; ++i) c += wv[mt][i] * relu(acc[mt][i]);
 #pragma unroll
                     for (int j = 0; j < NR; ++j)
                         if (j == rr) val[t][j] += c;
                 }
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
-                    if (H >= 8) val[t][j] += xor_lane_f(val[t][j], 16);
-                    if (H >= 16) val[t][j] += xor_lane_f(val[t][j], 32);
+                    if (H >= 8) val[t][j] = xor16_sum(val[t][j]);
+                    if (H >= 16) val[t][j] = xor32_sum(val[t][j]);
                 }
             }
         }
 
         // mask and store: lane writes column col0 + l%16 of each row it stores
+        float *orow[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) orow[j] = a.out + (int64_t)(row0 + st_rr[j]) * a.out_stride + c0;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int col0 = c0 + 16 * t;
             const bool live = col0 < vis;
-            const int col = col0 + (l & 15);
+            const int cc = 16 * t + (l & 15);  // column - c0
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
-                if (st_on[j] && col < a.width) {
+                if (st_on[j] && c0 + cc < a.width) {
                     const float v = live ? (ok[t] ? val[t][j] * kscale[t] : qnan) : neg_inf;
-                    a.out[(int64_t)(row0 + st_rr[j]) * a.out_stride + col] = col < st_ctx[j] ? v : neg_inf;
+                    orow[j][cc] = c0 + cc < st_ctx[j] ? v : neg_inf;
                 }
             }
         }
     }
+}
+
+// Looped variant for fp8 with 16+ heads: the MFMA work per key column is large
+// (H x RT rows), so the per-program set-up (row info, resident Q and weights)
+// and per-tile address work would otherwise dominate the instruction stream.
+// One program scores a long column range: `iters` groups of TPI key tiles, the
+// next group's keys in flight while the current group is scored (two register
+// buffers), the scores collected in LDS and every global store issued at the
+// end -- loads and stores share one memory counter on gfx9, so a store inside
+// the loop would hold up the next wait on keys.
+template <int H, int MT, int TPI, bool HAS_W, bool HAS_SCALE>
+__global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
+    typedef Frag<true> F;
+    constexpr int M = 16 * MT;
+    constexpr int RT = M / H;
+    static_assert(H >= 16 && RT >= 1 && RT <= 4, "looped variant: H >= 16, at most 4 rows");
+    constexpr int kMaxCols = 16 * TPI * 32;  // columns per program at most (iters <= 32)
+    __shared__ float obuf[RT][kMaxCols];
+
+    const int l = lane_id();
+    const int g = l >> 4;
+    const int tile = blockIdx.x / a.num_chunks;
+    const int chunk = blockIdx.x - tile * a.num_chunks;
+    const int row0 = tile * RT;
+    const int ncols = 16 * TPI * a.iters;
+    const int c0 = chunk * ncols;
+
+    int ctx_r[RT], req_r[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int row = min(row0 + r, a.num_rows - 1);
+        ctx_r[r] = a.ctx_lens[row];
+        req_r[r] = a.row_to_req[row];
+    }
+    uint32_t todo = 0u;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const bool valid = row0 + r < a.num_rows;
+        ctx_r[r] = valid ? min(max(ctx_r[r], 0), a.cap) : 0;
+        req_r[r] = valid ? req_r[r] : -1;
+        todo |= (valid ? 1u : 0u) << r;
+    }
+    typename F::T qa[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + (l & 15);
+        const int row = row0 + m / H, h = m % H;
+        const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) + ((int64_t)row * H + h) * F::kRowBytes;
+        qa[mt] = (row < a.num_rows) ? F::load(qrow + F::lane_bytes(l), 0) : F::zero();
+    }
+    float wv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * mt + 4 * g + i;
+            const int row = row0 + m / H, h = m % H;
+            wv[mt][i] = (HAS_W && row < a.num_rows) ? a.w[(int64_t)row * H + h] : 1.0f;
+        }
+
+    const float neg_inf = -__builtin_inff();
+    const float qnan = __builtin_nanf("");
+    while (todo) {
+        const int r0 = __builtin_ctz(todo);
+        int req = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) req = (r == r0) ? req_r[r] : req;
+        uint32_t set = 0u;
+        int vis = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (((todo >> r) & 1u) && req_r[r] == req) {
+                set |= 1u << r;
+                vis = max(vis, ctx_r[r]);
+            }
+        }
+        todo &= ~set;
+        const bool req_ok = req >= 0 && req < a.num_reqs;
+        const int32_t *bt = a.block_table + (req_ok ? (int64_t)req * a.max_blocks : 0);
+
+        if (c0 < vis) {
+            // Three-stage pipeline over groups of TPI key tiles: block-table
+            // entries (scalar loads) two groups ahead, keys and scales one
+            // group ahead, scoring of the current group.  A tile past the
+            // visible range or with an out-of-range table entry loads from
+            // block 0 and is not scored.
+            const int lane_key = (l & 15) * (int)a.key_stride + F::lane_bytes(l);
+            // the table stage and the key stage each walk the columns with a cursor
+            ColCursor tab(c0, a.block_size), key(c0, a.block_size);
+            auto fetch_table = [&](int (&blk)[TPI]) {
+#pragma unroll
+                for (int t = 0; t < TPI; ++t) {
+                    blk[t] = req_ok ? bt[min(tab.q, a.max_blocks - 1)] : -1;
+                    tab.step(a.block_size);
+                }
+            };
+            auto load_group = [&](int cg, const int (&blk)[TPI], typename F::T (&b)[TPI], float (&sc)[TPI],
+                                  bool (&ok)[TPI]) {
+#pragma unroll
+                for (int t = 0; t < TPI; ++t) {
+                    const int col0 = cg + 16 * t;
+                    ok[t] = col0 < vis && blk[t] >= 0 && (int64_t)blk[t] < a.num_blocks;
+                    const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
+                    const int tslot = ok[t] ? key.r : 0;
+                    key.step(a.block_size);
+                    b[t] = F::load(a.kcache + bbase + (int64_t)tslot * a.key_stride + lane_key, 0);
+                    sc[t] = 1.0f;
+                    if (HAS_SCALE) {
+                        if (a.layout == 1)
+                            sc[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
+                        else
+                            sc[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
+                    }
+                }
+            };
+            // scores of one group into obuf
+            auto score_group = [&](int cg, const typename F::T (&b)[TPI], const float (&sc)[TPI],
+                                   const bool (&ok)[TPI]) {
+                // every MFMA of the group first, into its own accumulator, so the
+                // matrix unit streams while the reductions wait for results
+                f32x4 acc[TPI][MT];
+#pragma unroll
+                for (int t = 0; t < TPI; ++t)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = F::mma(qa[mt], b[t], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int t = 0; t < TPI; ++t) {
+                    float val[RT];
+#pragma unroll
+                    for (int j = 0; j < RT; ++j) val[j] = 0.0f;
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        float c = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) c += wv[mt][i] * relu(acc[t][mt][i]);
+                        val[(16 * mt) / H] += c;  // every slot of tile mt is in row 16mt/H
+                    }
+#pragma unroll
+                    for (int j = 0; j < RT; ++j) {
+                        val[j] = xor32_sum(xor16_sum(val[j]));
+                        // every lane group holds the sums: all write (no branch
+                        // splitting the group's schedule), equal values per address
+                        obuf[j][cg - c0 + 16 * t + (l & 15)] = ok[t] ? val[j] * sc[t] : qnan;
+                    }
+                }
+            };
+            constexpr int GC = 16 * TPI;  // columns per group
+            int tA[TPI], tB[TPI];
+            typename F::T bA[TPI], bB[TPI];
+            float sA[TPI], sB[TPI];
+            bool oA[TPI], oB[TPI];
+            fetch_table(tA);
+            fetch_table(tB);
+            load_group(c0, tA, bA, sA, oA);
+#pragma unroll 1
+            for (int it = 0; it < a.iters; it += 2) {  // iters is even
+                const int cg = c0 + GC * it;
+                load_group(cg + GC, tB, bB, sB, oB);  // (past the end: block 0, discarded)
+                fetch_table(tA);
+                score_group(cg, bA, sA, oA);
+                load_group(cg + 2 * GC, tA, bA, sA, oA);
+                fetch_table(tB);
+                score_group(cg + GC, bB, sB, oB);
+            }
+        }
+
+        // every store of the request's rows, from LDS (or -inf past the
+        // visible range): lane l writes 4 consecutive columns per step
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            if (!((set >> j) & 1u)) continue;
+            float *orow = a.out + (int64_t)(row0 + j) * a.out_stride;
+            const int ctx = ctx_r[j];
+            for (int cc = 4 * l; cc < ncols; cc += 256) {
+                const int col = c0 + cc;
+                if (col >= a.width) break;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (col + e < ctx && c0 < vis) ? obuf[j][cc + e] : neg_inf;
+                if (col + 3 < a.width) {
+                    *reinterpret_cast<f32x4 *>(orow + col) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < a.width) orow[col + e] = v[e];
+                }
+            }
+        }
+    }
+}
+
+template <int H, int MT, int TPI>
+hipError_t launch_looped(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
+    const bool has_w = a.w != nullptr;
+    const bool has_s = a.layout == 1 || a.kscale != nullptr;
+    if (has_w && has_s)
+        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, true, true>), grid, block, 0, s, e0, e1, 0, a);
+    else if (has_w)
+        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, true, false>), grid, block, 0, s, e0, e1, 0, a);
+    else if (has_s)
+        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, false, true>), grid, block, 0, s, e0, e1, 0, a);
+    else
+        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, false, false>), grid, block, 0, s, e0, e1, 0, a);
+    return hipGetLastError();
 }
 
 template <bool FP8, int H, int MT, int TPW>
@@ -318,8 +544,18 @@ hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_
 
 template <bool FP8>
 hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    // chunk width per program (tiles of 16 columns) follows plan_logits
-    (void)p;
+    // (heads, stacked tiles, tiles per program) as chosen by plan_logits
+    if constexpr (FP8) {
+        if (p.iters > 0) {  // looped variant (plan_logits: fp8, 16+ heads)
+            switch (a.num_heads * 4 + p.rows_per_tile) {
+                case 16 * 4 + 1: return launch_looped<16, 1, 4>(a, s, e0, e1);
+                case 16 * 4 + 4: return launch_looped<16, 4, 4>(a, s, e0, e1);
+                case 32 * 4 + 1: return launch_looped<32, 2, 4>(a, s, e0, e1);
+                case 64 * 4 + 1: return launch_looped<64, 4, 4>(a, s, e0, e1);
+                default: return hipErrorInvalidValue;
+            }
+        }
+    }
     switch (a.num_heads) {
         case 1: return launch_h<FP8, 1, 1, 4>(a, s, e0, e1);
         case 2: return launch_h<FP8, 2, 1, 4>(a, s, e0, e1);
@@ -334,11 +570,9 @@ hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,
 
 }  // namespace
 
-LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width) {
-    (void)dtype;
-    (void)num_rows;
-    (void)width;
+LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width) {
     LogitsPlan p;
+    p.iters = 0;
     p.m_tiles = num_heads > 16 ? num_heads / 16 : 1;
     p.rows_per_tile = 16 * p.m_tiles / num_heads;
     // 16-column tiles per program: 4 for the few-head decode shapes (a sweep on
@@ -346,6 +580,23 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width) {
     // key bytes per column (long single-row and many-head fp8 shapes gained
     // 3..15%)
     p.tiles_per_prog = num_heads <= 4 ? 4 : 8;
+    // fp8 with 16+ heads: the looped variant, 4 key tiles per group and as many
+    // groups per program as leave about four programs per SIMD; with 16 heads
+    // and several rows per request (MTP verify rows) 4 rows share a program
+    if (dtype == 1 && num_heads >= 16) {
+        const int rows_per_req = num_reqs > 0 ? num_rows / num_reqs : 1;
+        if (num_heads == 16 && rows_per_req >= 4) {
+            p.rows_per_tile = 4;
+            p.m_tiles = 4;
+        }
+        const int tpi = 4;
+        const int row_tiles = (num_rows + p.rows_per_tile - 1) / p.rows_per_tile;
+        const int col_tiles = (width + 15) / 16;
+        int iters = 32;
+        while (iters > 2 && (int64_t)row_tiles * ((col_tiles + tpi * iters - 1) / (tpi * iters)) < 4096) iters /= 2;
+        p.iters = iters;
+        p.tiles_per_prog = tpi * iters;
+    }
     return p;
 }
 

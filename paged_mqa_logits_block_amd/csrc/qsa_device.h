@@ -126,6 +126,29 @@ __device__ __forceinline__ uint32_t wave_total_umax(uint32_t v) {
     return (uint32_t)readlane(wave_scan_dpp((int)v, 0, OpMaxU()), 63);
 }
 
+// v + (v of lane l ^ 16) and v + (v of lane l ^ 32), each with one gfx950
+// lane-swap instruction and an add, no LDS round trip.  permlane16_swap(a, b)
+// exchanges the odd 16-lane rows of a with the even rows of b, and
+// permlane32_swap(a, b) the upper half of a with the lower half of b; with
+// a = b = v the two results hold, in every lane, v and its partner's v.
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// max(x, 0) for finite x in one instruction: v_med3_f32(x, 0, FLT_MAX).
+// fmaxf(x, 0) costs two (a NaN-quieting canonicalize of x first, as the
+// compiler cannot see that an MFMA result is never a signalling NaN), and a
+// +inf upper bound lets the compiler turn med3 back into that fmaxf.  Scores
+// are finite (bounded products of finite bf16 / fp8 inputs).
+__device__ __forceinline__ float relu(float x) {
+    return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e+38f);
+}
+
 // f32 bits -> u32 whose unsigned order is the float order; -0 is folded onto +0
 // so that the two zeros compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -34,6 +34,8 @@ struct LogitsArgs {
     int64_t block_bytes;    // stride between pool blocks
     int64_t key_stride;     // bytes between keys inside a block
     int64_t scale_offset;   // co-packed: byte offset of the scales inside a block
+    int32_t iters;          // looped variant: key-tile groups per program
+    int32_t pad2_;
 };
 
 // Variant chosen for a call: rows per tile and column tiles per program.
@@ -41,9 +43,10 @@ struct LogitsPlan {
     int rows_per_tile;
     int tiles_per_prog;  // 16-column tiles per program
     int m_tiles;         // 16-row MFMA tiles stacked per program
+    int iters;           // > 0: looped variant with this many key-tile groups
 };
 
-LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int width);
+LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width);
 // start / stop (may be null) are recorded by the dispatch packet itself at the
 // kernel's start and end.
 hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,

@@ -98,6 +98,24 @@ def test_heads_and_dtypes(H, dtype, layout):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"H{H}")
 
 
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("layout", ["paged", "copacked"])
+@pytest.mark.parametrize("req_rows", [(4, 4, 4, 4), (5, 3, 6, 2)])
+def test_fp8_many_heads_mtp_rows(H, layout, req_rows):
+    """fp8, 16+ heads, 4+ rows per request (the MTP verify shape): ragged ctx
+    within a request, requests of unequal row counts, a width that ends inside
+    a key tile, poisoned table slots and key tails."""
+    n = sum(req_rows)
+    base = [1000, 997, 998, 999, 65, 64, 63, 0, 3000, 2999, 2998, 2997, 16, 17, 15, 1]
+    ctx = [base[i % len(base)] for i in range(n)]
+    inp = qsa_inputs.build(name="stack", seed=700 + H + n, req_rows=list(req_rows), ctx_rows=ctx,
+                           num_heads=H, block_size=64, dtype="fp8", layout=layout,
+                           weights=(H != 32), width=3004, poison=True)
+    say("fp8 mtp rows", H, layout, req_rows)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"mtp H{H}")
+
+
 @pytest.mark.parametrize("B", [16, 32, 64, 128, 1024])
 def test_block_sizes_and_ragged_ctx(B):
     ctx = [1, B - 1, B, B + 1, 3 * B + 5, 2047, 2048, 2049]
