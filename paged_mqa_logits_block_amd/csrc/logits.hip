@@ -526,6 +526,226 @@ hipError_t launch_looped(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipE
     return hipGetLastError();
 }
 
+// Prefill variant (bf16, 4 heads, one request holding many rows): every row
+// tile reads the whole key range of the request, so rows are stacked wide and
+// keys streamed through the 32x32x16 bf16 MFMA (twice the rate of the
+// 16x16x32 form on gfx950).
+//
+// A workgroup of NW waves owns 16 NW rows and walks its column range 32
+// columns (one 8 KB run of keys inside one pool block) at a time.  The run is
+// fetched once per workgroup with contiguous 16-byte loads and written to LDS
+// with each key padded to 272 bytes; the waves then read their MFMA
+// fragments from LDS without bank conflicts.  (Fragment loads straight from
+// global memory would touch a different cache line in every lane.)  Runs are
+// fetched two steps ahead and double-buffered in LDS, one barrier per step.
+//
+// Each wave holds its 16 rows as 64 stacked (row, head) pairs in two 32-row M
+// tiles with Q resident.  The 32x32 accumulator gives lane l the 4 heads of
+// rows 2q + l/32 (q = 0..3) of each M tile for column l % 32, so the head sum
+// is in-lane.  K step s of the MFMA takes elements 16 s + 8 (l / 32) + 0..7
+// of the head dimension on both operands.
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t pf_u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPfKeyLds = 272;           // padded key in LDS (bytes)
+constexpr int kPfRunLds = 32 * kPfKeyLds;  // one 32-key run
+
+template <bool HAS_W, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_logits_kernel(LogitsArgs a) {
+    constexpr int H = 4;
+    constexpr int NT = 64 * NW;           // threads
+    constexpr int LPT = 8192 / (16 * NT);  // 16-byte loads per thread per run
+    static_assert(LPT >= 1 && LPT * 16 * NT == 8192, "a run is 8 KB");
+    __shared__ __align__(16) uint8_t kbuf[2][kPfRunLds];
+
+    const int t = threadIdx.x;
+    const int l = lane_id();
+    const int gk = l >> 5;  // lane half
+    const int w = t >> 6;
+    const int rb = blockIdx.x / a.num_chunks;
+    const int chunk = blockIdx.x - rb * a.num_chunks;
+    const int row0 = rb * 16 * NW + w * 16;  // this wave's 16 rows
+    const int c0 = chunk * 32 * a.iters;
+    if (c0 >= a.width) return;  // the whole workgroup
+    const int nsteps = min(a.iters, (a.width - c0 + 31) / 32);
+    // a wave past the last row still takes part in the fetches and barriers
+    const bool active = row0 < a.num_rows;
+
+    // Rows of the wave (lane j < 16: row row0 + j).  A row past the last one
+    // takes the last row's place everywhere (Q, weights, visible count, output
+    // row): it computes and stores the same values to the same addresses, so
+    // no store needs a per-row mask.  There is one request; a row whose
+    // row_to_req names anything else reads no keys and its visible columns
+    // are written as NaN.
+    int ctx_l, rok_l;
+    {
+        const int row = min(row0 + (l & 15), a.num_rows - 1);
+        ctx_l = min(max(a.ctx_lens[row], 0), a.cap);
+        rok_l = a.row_to_req[row] == 0;
+    }
+    int vis = ctx_l;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) vis = max(vis, xor_lane_i(vis, m));
+    vis = readlane(vis, 0);
+    // visible range of the workgroup: how far the key runs are fetched
+    int vis_wg = 0;
+    for (int r = l; r < 16 * NW; r += 64) {
+        const int row = min(rb * 16 * NW + r, a.num_rows - 1);
+        vis_wg = max(vis_wg, min(max(a.ctx_lens[row], 0), a.cap));
+    }
+    vis_wg = readlane(wave_max_i(vis_wg), 0);
+
+    // resident Q: A operand of M tile mt, K step s: stacked pair 32 mt + l%32
+    pf_bf16x8 qa[2][8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int m = 32 * mt + (l & 31);
+        const int row = min(row0 + m / H, a.num_rows - 1), h = m % H;
+        const __bf16 *qr = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)row * H + h) * kD + 8 * gk;
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) qa[mt][s2] = *reinterpret_cast<const pf_bf16x8 *>(qr + 16 * s2);
+    }
+    // Accumulator slot 4q + h of M tile mt holds head h of wave row
+    // 8 mt + 2 q + gk for column l % 32: its weight, visible count, request
+    // check and output row.
+    float wv[2][4][4];
+    int ctx_q[2][4];
+    bool rok_q[2][4];
+    float *orow[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = 8 * mt + 2 * q;
+            const int row = min(row0 + j + gk, a.num_rows - 1);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) wv[mt][q][h] = HAS_W ? a.w[(int64_t)row * H + h] : 1.0f;
+            ctx_q[mt][q] = gk ? readlane(ctx_l, j + 1) : readlane(ctx_l, j);
+            rok_q[mt][q] = (gk ? readlane(rok_l, j + 1) : readlane(rok_l, j)) != 0;
+            orow[mt][q] = a.out + (int64_t)row * a.out_stride;
+        }
+
+    const float neg_inf = -__builtin_inff();
+    const float qnan = __builtin_nanf("");
+    const int32_t *bt = a.block_table;
+    // Table cursor of the run fetched next (block_size is a multiple of 32, so
+    // a run lies in one pool block), and the table entry of the run after it.
+    int tq = c0 / a.block_size, tr = c0 - tq * a.block_size;
+    int ent = bt[min(tq, a.max_blocks - 1)];
+    int ent_next = bt[min(tq + (tr + 32 >= a.block_size ? 1 : 0), a.max_blocks - 1)];
+    int cl = c0;  // first column of the run fetched next
+
+    // fetch the next run into registers (past the visible range: the first
+    // run of block 0, always in the pool, never scored)
+    auto fetch = [&](pf_u32x4 (&r)[LPT]) -> bool {
+        const bool ok = cl < vis_wg && ent >= 0 && (int64_t)ent < a.num_blocks;
+        const uint8_t *kt = a.kcache + (ok ? (int64_t)ent * a.block_bytes + (int64_t)tr * a.key_stride : 0);
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) r[i] = *reinterpret_cast<const pf_u32x4 *>(kt + 16 * (t + NT * i));
+        cl += 32;
+        tr += 32;
+        const bool wrap = tr >= a.block_size;
+        tr = wrap ? tr - a.block_size : tr;
+        tq = wrap ? tq + 1 : tq;
+        ent = ent_next;
+        ent_next = bt[min(tq + (tr + 32 >= a.block_size ? 1 : 0), a.max_blocks - 1)];
+        return ok;
+    };
+    // byte e of the run (key e / 256, byte e % 256) goes to key slot e / 256
+    auto put = [&](uint8_t *buf, const pf_u32x4 (&r)[LPT]) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int e = 16 * (t + NT * i);
+            *reinterpret_cast<pf_u32x4 *>(buf + (e >> 8) * kPfKeyLds + (e & 255)) = r[i];
+        }
+    };
+    // MFMAs of the run held in buf
+    auto mfma_run = [&](const uint8_t *buf, f32x16 (&acc)[2]) {
+        pf_bf16x8 b[8];
+        const uint8_t *kf = buf + (l & 31) * kPfKeyLds + 16 * gk;
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) b[s2] = *reinterpret_cast<const pf_bf16x8 *>(kf + 32 * s2);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            acc[mt] = f32x16{};
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s2], b[s2], acc[mt], 0, 0, 0);
+        }
+    };
+    // head sum, masks and stores of the run at column cg (scored: acc holds
+    // its MFMA results)
+    auto finish = [&](int cg, bool scored, const f32x16 (&acc)[2], bool ok) {
+        const int col = cg + (l & 31);
+        float val[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v = 0.0f;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) v += wv[mt][q][h] * relu(acc[mt][4 * q + h]);
+                const float x = (ok & rok_q[mt][q]) ? v : qnan;
+                val[mt][q] = (scored & (col < ctx_q[mt][q])) ? x : neg_inf;
+            }
+        if (col < a.width) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) orow[mt][q][col] = val[mt][q];
+        }
+    };
+
+    // One step: fetch the run two ahead; MFMAs of this run (from LDS); write
+    // the run one ahead to the other LDS buffer -- after the MFMAs, so the wait
+    // on its fetch (which also covers the previous step's stores, loads and
+    // stores sharing one counter) finds them done; then this run's stores;
+    // one barrier.
+    pf_u32x4 rA[LPT], rB[LPT];
+    bool ok0 = fetch(rA);  // run 0
+    bool ok1 = fetch(rB);  // run 1
+    put(kbuf[0], rA);
+    __syncthreads();
+    f32x16 acc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) acc[mt] = f32x16{};
+    // pairs of runs (run st in kbuf[0], run st + 1 in rB at the top), then an
+    // odd last run
+    int st = 0;
+#pragma unroll 1
+    for (; st + 1 < nsteps; st += 2) {
+        const int cg = c0 + 32 * st;
+        const bool ok2 = fetch(rA);  // run st + 2
+        const bool sc0 = active & (cg < vis);
+        if (sc0) mfma_run(kbuf[0], acc);
+        put(kbuf[1], rB);
+        if (active) finish(cg, sc0, acc, ok0);
+        __syncthreads();
+        const bool ok3 = fetch(rB);  // run st + 3
+        const bool sc1 = active & (cg + 32 < vis);
+        if (sc1) mfma_run(kbuf[1], acc);
+        put(kbuf[0], rA);
+        if (active) finish(cg + 32, sc1, acc, ok1);
+        __syncthreads();
+        ok0 = ok2;
+        ok1 = ok3;
+    }
+    if (st < nsteps) {
+        const int cg = c0 + 32 * st;
+        const bool sc0 = active & (cg < vis);
+        if (sc0) mfma_run(kbuf[0], acc);
+        if (active) finish(cg, sc0, acc, ok0);
+    }
+}
+
+template <bool HAS_W_, int NW>
+static hipError_t launch_prefill_w(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64 * NW);
+    hipExtLaunchKernelGGL((prefill_logits_kernel<HAS_W_, NW>), grid, block, 0, s, e0, e1, 0, a);
+    return hipGetLastError();
+}
+
 template <bool FP8, int H, int MT, int TPW>
 hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
@@ -545,6 +765,11 @@ hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_
 template <bool FP8>
 hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     // (heads, stacked tiles, tiles per program) as chosen by plan_logits
+    if constexpr (!FP8) {
+        if (p.prefill)
+            return a.w ? launch_prefill_w<true, kPrefillWaves>(a, s, e0, e1)
+                       : launch_prefill_w<false, kPrefillWaves>(a, s, e0, e1);
+    }
     if constexpr (FP8) {
         if (p.iters > 0) {  // looped variant (plan_logits: fp8, 16+ heads)
             switch (a.num_heads * 4 + p.rows_per_tile) {
@@ -570,9 +795,25 @@ hipError_t launch_dtype(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,
 
 }  // namespace
 
-LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width) {
+LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width, int block_size) {
     LogitsPlan p;
     p.iters = 0;
+    p.prefill = false;
+    // bf16, 4 heads, a single request holding all rows (a prefill chunk), pool
+    // blocks of a multiple of 32 columns: the prefill variant, 64 rows per
+    // workgroup, columns split so that about two workgroups run per CU
+    if (dtype == 0 && num_heads == 4 && num_reqs == 1 && num_rows >= 256 && block_size % 32 == 0) {
+        p.prefill = true;
+        p.rows_per_tile = 16 * kPrefillWaves;
+        p.m_tiles = 1;
+        const int row_tiles = (num_rows + p.rows_per_tile - 1) / p.rows_per_tile;
+        const int steps = (width + 31) / 32;
+        int splits = 1;
+        while (splits < steps && (int64_t)row_tiles * splits * kPrefillWaves < 2048) splits *= 2;
+        p.iters = (steps + splits - 1) / splits;
+        p.tiles_per_prog = 2 * p.iters;  // in 16-column tiles
+        return p;
+    }
     p.m_tiles = num_heads > 16 ? num_heads / 16 : 1;
     p.rows_per_tile = 16 * p.m_tiles / num_heads;
     // 16-column tiles per program: 4 for the few-head decode shapes (a sweep on

@@ -44,9 +44,14 @@ struct LogitsPlan {
     int tiles_per_prog;  // 16-column tiles per program
     int m_tiles;         // 16-row MFMA tiles stacked per program
     int iters;           // > 0: looped variant with this many key-tile groups
+                         // (prefill variant: 32-column steps per program)
+    bool prefill;        // prefill variant (bf16, 4 heads, one request)
 };
 
-LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width);
+// waves per workgroup of the prefill variant (16 rows each)
+constexpr int kPrefillWaves = 8;
+
+LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width, int block_size);
 // start / stop (may be null) are recorded by the dispatch packet itself at the
 // kernel's start and end.
 hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,

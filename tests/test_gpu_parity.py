@@ -126,6 +126,65 @@ def test_block_sizes_and_ragged_ctx(B):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"B{B}")
 
 
+def _prefill_ctx(n, W, seed):
+    """Causal visible counts of a chunk of n rows ending at column W, with
+    edge counts mixed in (0, 1, a step boundary and its neighbours, past the
+    width)."""
+    rng = np.random.default_rng(seed)
+    ctx = (W - n + 1 + np.arange(n)).astype(np.int64)
+    ctx = np.minimum(ctx, W)
+    edges = [0, 1, 31, 32, 33, 63, 64, 65, W - 1, W, W + 100]
+    at = rng.choice(n, size=len(edges), replace=False)
+    ctx[at] = edges
+    return ctx
+
+
+@pytest.mark.parametrize("B", [32, 64, 128])
+@pytest.mark.parametrize("weights", [True, False])
+def test_prefill_many_rows_one_request(B, weights):
+    """bf16, 4 heads, one request holding a few hundred rows (the prefill
+    chunk shape, its own kernel): ragged row count and width, edge visible
+    counts, poisoned table slots and key tails."""
+    n, W = 333, 1000
+    ctx = _prefill_ctx(n, W, seed=B)
+    inp = qsa_inputs.build(name="prefill", seed=900 + B, req_rows=[n], ctx_rows=ctx, kv_lens=[W],
+                           num_heads=4, block_size=B, width=W, weights=weights, poison=True)
+    say("prefill rows", n, "width", W, "block", B, "weights", weights)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"prefill B{B}")
+
+
+def test_prefill_long_column_range():
+    """Prefill kernel with several 32-column steps per program (an odd count)
+    and a width that ends inside a step."""
+    n, W = 300, 20012
+    ctx = _prefill_ctx(n, W, seed=7)
+    inp = qsa_inputs.build(name="prefill", seed=951, req_rows=[n], ctx_rows=ctx, kv_lens=[W],
+                           num_heads=4, block_size=64, width=W, weights=True, poison=True)
+    say("prefill long rows", n, "width", W)
+    _, g = run_logits(inp)
+    rows = list(range(0, n, 7)) + [n - 1]
+    x = g.cpu().numpy()[rows]
+    assert_logits_match(x, oracle.paged_logits(inp, rows=rows), inp, rows, label="prefill long")
+
+
+def test_prefill_invalid_table_entry_and_request_give_nan():
+    n, W = 260, 512
+    inp = qsa_inputs.build(name="prefill bad", seed=952, req_rows=[n], ctx_rows=[300] * n,
+                           kv_lens=[W], num_heads=4, block_size=64, width=W)
+    inp.block_table[0, 2] = inp.num_blocks + 3  # columns 128..191
+    inp.row_to_req = inp.row_to_req.copy()
+    inp.row_to_req[[5, 200]] = 1  # only request 0 exists
+    say("prefill invalid table entry / request")
+    _, g = run_logits(inp)
+    x = g.cpu().numpy()
+    ok = np.ones(n, bool)
+    ok[[5, 200]] = False
+    assert np.all(np.isnan(x[ok][:, 128:192])) and np.all(np.isfinite(x[ok][:, :128]))
+    assert np.all(np.isfinite(x[ok][:, 192:300])) and np.all(x[:, 300:] == -np.inf)
+    assert np.all(np.isnan(x[~ok][:, :300]))
+
+
 def test_rows_spanning_requests_and_shuffled():
     # one row per request, and rows of one request scattered over tiles
     ctx = list(range(100, 100 + 37 * 13, 13))
