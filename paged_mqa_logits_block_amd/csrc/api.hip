@@ -127,7 +127,8 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     if (s->num_rows == 0 || s->width == 0) return ok();
     const bool fp8 = s->k_dtype == QSA_FP8_E4M3FN;
     const int64_t elt = fp8 ? 1 : 2;
-    qsa::LogitsPlan plan = qsa::plan_logits(fp8 ? 1 : 0, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size);
+    qsa::LogitsPlan plan = qsa::plan_logits(fp8 ? 1 : 0, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
+                                                s->out_stride);
     qsa::LogitsArgs a = {};
     a.q = q;
     a.w = w;

@@ -48,10 +48,14 @@ struct LogitsPlan {
     bool prefill;        // prefill variant (bf16, 4 heads, one request)
 };
 
-// waves per workgroup of the prefill variant (16 rows each)
+// consumer waves per workgroup of the prefill variant (16 rows each; one
+// producer wave besides), and how many of its workgroups one CU holds at once
+// (VGPR-bound: 3 waves per SIMD)
 constexpr int kPrefillWaves = 8;
+constexpr int kPrefillGroupsPerCU = 12 / (kPrefillWaves + 1);
 
-LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width, int block_size);
+LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width, int block_size,
+                       int64_t out_stride);
 // start / stop (may be null) are recorded by the dispatch packet itself at the
 // kernel's start and end.
 hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,
