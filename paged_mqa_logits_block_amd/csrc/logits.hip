@@ -328,7 +328,10 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
 // buffers), the scores collected in LDS and every global store issued at the
 // end -- loads and stores share one memory counter on gfx9, so a store inside
 // the loop would hold up the next wait on keys.
-template <int H, int MT, int TPI, bool HAS_W, bool HAS_SCALE>
+// ONE_BLOCK: block_size is a multiple of the group's 16 TPI columns, so every
+// group lies in one pool block (group starts are multiples of 16 TPI): one
+// table entry and one base address per group, the tiles at fixed offsets.
+template <int H, int MT, int TPI, bool HAS_W, bool HAS_SCALE, bool ONE_BLOCK>
 __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
     typedef Frag<true> F;
     constexpr int M = 16 * MT;
@@ -408,28 +411,57 @@ __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
             // the table stage and the key stage each walk the columns with a cursor
             ColCursor tab(c0, a.block_size), key(c0, a.block_size);
             auto fetch_table = [&](int (&blk)[TPI]) {
+                if (ONE_BLOCK) {
+                    blk[0] = req_ok ? bt[min(tab.q, a.max_blocks - 1)] : -1;
+                    // next group: the same block or the next one
+                    tab.r += 16 * TPI;
+                    const bool wrap = tab.r >= a.block_size;
+                    tab.r = wrap ? 0 : tab.r;
+                    tab.q = wrap ? tab.q + 1 : tab.q;
+                } else {
 #pragma unroll
-                for (int t = 0; t < TPI; ++t) {
-                    blk[t] = req_ok ? bt[min(tab.q, a.max_blocks - 1)] : -1;
-                    tab.step(a.block_size);
+                    for (int t = 0; t < TPI; ++t) {
+                        blk[t] = req_ok ? bt[min(tab.q, a.max_blocks - 1)] : -1;
+                        tab.step(a.block_size);
+                    }
                 }
             };
             auto load_group = [&](int cg, const int (&blk)[TPI], typename F::T (&b)[TPI], float (&sc)[TPI],
                                   bool (&ok)[TPI]) {
+                if (ONE_BLOCK) {
+                    const bool bok = (blk[0] >= 0) & ((int64_t)blk[0] < a.num_blocks);
+                    const int64_t bbase = bok ? (int64_t)blk[0] * a.block_bytes : 0;
+                    const int slot0 = bok ? key.r : 0;
+                    key.r += 16 * TPI;
+                    const bool wrap = key.r >= a.block_size;
+                    key.r = wrap ? 0 : key.r;
+                    const uint8_t *kb = a.kcache + bbase + (int64_t)slot0 * F::kRowBytes + lane_key;
+                    const float *sb = HAS_SCALE ? (a.layout == 1 ? reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)
+                                                                 : a.kscale + (bok ? (int64_t)blk[0] * a.block_size : 0))
+                                                 + slot0 + (l & 15)
+                                                : nullptr;
 #pragma unroll
-                for (int t = 0; t < TPI; ++t) {
-                    const int col0 = cg + 16 * t;
-                    ok[t] = col0 < vis && blk[t] >= 0 && (int64_t)blk[t] < a.num_blocks;
-                    const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
-                    const int tslot = ok[t] ? key.r : 0;
-                    key.step(a.block_size);
-                    b[t] = F::load(a.kcache + bbase + (int64_t)tslot * a.key_stride + lane_key, 0);
-                    sc[t] = 1.0f;
-                    if (HAS_SCALE) {
-                        if (a.layout == 1)
-                            sc[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
-                        else
-                            sc[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
+                    for (int t = 0; t < TPI; ++t) {
+                        ok[t] = bok & (cg + 16 * t < vis);
+                        b[t] = F::load(kb + 16 * t * F::kRowBytes, 0);
+                        sc[t] = HAS_SCALE ? sb[16 * t] : 1.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < TPI; ++t) {
+                        const int col0 = cg + 16 * t;
+                        ok[t] = (col0 < vis) & (blk[t] >= 0) & ((int64_t)blk[t] < a.num_blocks);
+                        const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
+                        const int tslot = ok[t] ? key.r : 0;
+                        key.step(a.block_size);
+                        b[t] = F::load(a.kcache + bbase + (int64_t)tslot * a.key_stride + lane_key, 0);
+                        sc[t] = 1.0f;
+                        if (HAS_SCALE) {
+                            if (a.layout == 1)
+                                sc[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
+                            else
+                                sc[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
+                        }
                     }
                 }
             };
@@ -510,19 +542,27 @@ __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
     }
 }
 
+template <int H, int MT, int TPI, bool HAS_W, bool HAS_SCALE>
+static void launch_looped_b(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
+    if (a.block_size % (16 * TPI) == 0)
+        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, HAS_W, HAS_SCALE, true>), grid, block, 0, s, e0, e1, 0, a);
+    else
+        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, HAS_W, HAS_SCALE, false>), grid, block, 0, s, e0, e1, 0, a);
+}
+
 template <int H, int MT, int TPI>
 hipError_t launch_looped(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
     const bool has_s = a.layout == 1 || a.kscale != nullptr;
     if (has_w && has_s)
-        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, true, true>), grid, block, 0, s, e0, e1, 0, a);
+        launch_looped_b<H, MT, TPI, true, true>(a, s, e0, e1);
     else if (has_w)
-        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, true, false>), grid, block, 0, s, e0, e1, 0, a);
+        launch_looped_b<H, MT, TPI, true, false>(a, s, e0, e1);
     else if (has_s)
-        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, false, true>), grid, block, 0, s, e0, e1, 0, a);
+        launch_looped_b<H, MT, TPI, false, true>(a, s, e0, e1);
     else
-        hipExtLaunchKernelGGL((looped_logits_kernel<H, MT, TPI, false, false>), grid, block, 0, s, e0, e1, 0, a);
+        launch_looped_b<H, MT, TPI, false, false>(a, s, e0, e1);
     return hipGetLastError();
 }
 
