@@ -69,6 +69,19 @@ def algorithmic_bytes(inp):
     return reads, writes
 
 
+def scoring_kernel(inp):
+    """The scoring kernel the library picks for this shape (the same rule as
+    its planner): the prefill variant for bf16, 4 heads and one request with
+    256+ rows and blocks of a multiple of 32 columns; the looped variant for
+    fp8 with 16+ heads; the per-tile variant otherwise."""
+    if (inp.dtype == "bf16" and inp.num_heads == 4 and inp.num_reqs == 1 and inp.num_rows >= 256
+            and inp.block_size % 32 == 0):
+        return "prefill_logits_kernel"
+    if inp.dtype == "fp8" and inp.num_heads >= 16:
+        return "looped_logits_kernel"
+    return "paged_logits_kernel"
+
+
 def source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -226,7 +239,7 @@ def main():
         "topk_us": round(topk_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "paged_logits_kernel", "algorithmic_bytes": per_call,
+                     "kernel": scoring_kernel(inp), "algorithmic_bytes": per_call,
                      "algorithmic_read_bytes": reads, "algorithmic_write_bytes": writes},
     }
     if not args.no_cpu_baseline:
