@@ -46,7 +46,12 @@ struct LogitsPlan {
     int iters;           // > 0: looped variant with this many key-tile groups
                          // (prefill variant: 32-column steps per program)
     bool prefill;        // prefill variant (bf16, 4 heads, one request)
+    bool mtp;            // 4-row fp8 variant (32/64 heads; iters = 64-column runs per program)
 };
+
+// 4-row fp8 variant: columns per key run, runs per program at most
+constexpr int kMtpRunCols = 64;
+constexpr int kMtpMaxRunsPerGroup = 16;
 
 // consumer waves per workgroup of the prefill variant (16 rows each; one
 // producer wave besides), and how many of its workgroups one CU holds at once

@@ -116,6 +116,51 @@ def test_fp8_many_heads_mtp_rows(H, layout, req_rows):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"mtp H{H}")
 
 
+@pytest.mark.parametrize("H", [32, 64])
+@pytest.mark.parametrize("layout", ["paged", "copacked"])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_fp8_four_row_requests(H, layout, shuffle):
+    """fp8, 32/64 heads, exactly 4 rows per request (the 4-row workgroup
+    variant): ragged ctx inside a request, a width ending inside a key run,
+    blocks of 64 and 128 columns, poisoned table slots and key tails; with
+    shuffle the rows of a request are scattered over tiles (tiles whose rows
+    belong to several requests)."""
+    reqs = 6
+    base = [3000, 2999, 2998, 2997, 65, 64, 63, 0, 1000, 997, 998, 999, 129, 128, 127, 1,
+            1500, 1499, 1498, 1497, 2048, 2047, 2046, 2045]
+    ctx = base[:4 * reqs]
+    B = 64 if H == 64 else 128
+    inp = qsa_inputs.build(name="mtp4", seed=800 + H + (7 if shuffle else 0), req_rows=[4] * reqs,
+                           ctx_rows=ctx, num_heads=H, block_size=B, dtype="fp8", layout=layout,
+                           weights=True, width=3004, poison=True, shuffle_rows=shuffle)
+    say("fp8 4-row requests", H, layout, "shuffle", shuffle)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"mtp4 H{H}")
+
+
+def test_fp8_four_row_requests_long():
+    """The 4-row fp8 variant at a size where each workgroup walks several key
+    runs (16 requests x 16,384 columns: 4 runs of 64 columns per workgroup,
+    one full turn of the fetch ring), with an invalid table entry and an
+    invalid request (NaN); the oracle checks sampled rows."""
+    reqs, W = 16, 16384
+    ctx = [W - (i % 4) * 37 for i in range(4 * reqs)]
+    inp = qsa_inputs.build(name="mtp4 long", seed=880, req_rows=[4] * reqs, ctx_rows=ctx, kv_lens=[W] * reqs,
+                           num_heads=64, block_size=64, dtype="fp8", layout="copacked", weights=True,
+                           width=W)
+    inp.block_table[1, 5] = inp.num_blocks + 2  # columns 320..383 of request 1
+    inp.row_to_req = inp.row_to_req.copy()
+    inp.row_to_req[10] = reqs + 3  # past the table
+    say("fp8 4-row long, invalid entry / request")
+    _, g = run_logits(inp)
+    x = g.cpu().numpy()
+    assert np.all(np.isnan(x[4:8, 320:384])) and np.all(np.isfinite(x[4:8, :320]))
+    assert np.all(np.isnan(x[10, :ctx[10]])) and np.all(x[10, ctx[10]:] == -np.inf)
+    rows = [0, 1, 2, 3, 8, 9, 11, 30, 63]
+    o = oracle.paged_logits(inp, rows=rows)
+    assert_logits_match(x[rows], o, inp, rows, label="mtp4 long")
+
+
 @pytest.mark.parametrize("B", [16, 32, 64, 128, 1024])
 def test_block_sizes_and_ragged_ctx(B):
     ctx = [1, B - 1, B, B + 1, 3 * B + 5, 2047, 2048, 2049]
