@@ -699,13 +699,17 @@ __global__ __launch_bounds__(256) void mtp_fp8_kernel(LogitsArgs a) {
                 for (int tt = 0; tt < 4; ++tt) {
                     const typename F::T b =
                         *reinterpret_cast<const typename F::T *>(kbuf[buf] + tt * 16 * kMtpKeyLds + frag);
+                    // the tile's MFMAs first, into separate accumulators (one
+                    // reused accumulator would serialise each MFMA behind the
+                    // head sums of the one before)
+                    f32x4 acc[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = F::mma(qa[mt], b, f32x4{0.f, 0.f, 0.f, 0.f});
                     float val = 0.0f;
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const f32x4 acc = F::mma(qa[mt], b, f32x4{0.f, 0.f, 0.f, 0.f});
+                    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) val += wv[mt][i] * relu(acc[i]);
-                    }
+                        for (int i = 0; i < 4; ++i) val += wv[mt][i] * relu(acc[mt][i]);
                     val = xor32_sum(xor16_sum(val));
                     const float sc = HAS_SCALE ? sbuf[buf][16 * tt + (l & 15)] : 1.0f;
                     // every lane group holds the sum: all write, equal values
