@@ -667,9 +667,12 @@ __global__ __launch_bounds__(256) void mtp_fp8_kernel(LogitsArgs a) {
                 (req_ok ? (int64_t)req * a.max_blocks : 0);
             int tq = c0 / a.block_size, tr = c0 - tq * a.block_size;  // run cursor
             int cl = c0;
+            // runs the ring fetches past this workgroup's last one read block 0
+            // (cached), not the next chunk's keys
+            const int cend = min(vis, c0 + kMtpRun * nruns);
             auto fetch = [&](i32x8 &kr, float &sr) -> bool {
                 const int blk = req_ok ? bt[min(tq, a.max_blocks - 1)] : -1;
-                const bool ok = (cl < vis) & (blk >= 0) & ((int64_t)blk < a.num_blocks);
+                const bool ok = (cl < cend) & (blk >= 0) & ((int64_t)blk < a.num_blocks);
                 const int64_t bbase = ok ? (int64_t)blk * a.block_bytes : 0;
                 const int slot = ok ? tr : 0;
                 kr = *reinterpret_cast<const i32x8 *>(a.kcache + bbase + (int64_t)slot * F::kRowBytes + 32 * t);
