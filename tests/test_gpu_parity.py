@@ -279,6 +279,34 @@ def test_untouched_stride_tail_and_nan_canaries():
     assert_logits_match(b[:, : inp.width], oracle.paged_logits(inp), inp, label="stride")
 
 
+@pytest.mark.parametrize("kind", ["prefill", "fp8_4row"])
+def test_untouched_stride_tail_new_variants(kind):
+    """Padded output rows for the prefill and 4-row fp8 variants: the columns
+    between the width and the stride keep their NaN canaries (the prefill
+    variant's range-checked stores drop lanes past the width), and the first
+    canary column past the last row is untouched too."""
+    if kind == "prefill":
+        n, W = 300, 1000 + 4
+        inp = qsa_inputs.build(name="prefill stride", seed=961, req_rows=[n], ctx_rows=_prefill_ctx(n, W, 3),
+                               kv_lens=[W], num_heads=4, block_size=64, width=W, poison=True)
+    else:
+        inp = qsa_inputs.build(name="fp8 4-row stride", seed=962, req_rows=[4] * 5,
+                               ctx_rows=[1000, 999, 998, 997] * 5, num_heads=64, block_size=64, dtype="fp8",
+                               layout="copacked", weights=True, width=1004, poison=True)
+    dev = to_device(inp)
+    stride = inp.width + 44
+    buf = torch.full((inp.num_rows + 1, stride), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[: inp.num_rows, : inp.width]
+    say("stride tail", kind)
+    gpu_logits(inp, dev, out=out)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(np.isnan(b[: inp.num_rows, inp.width:]))
+    assert np.all(np.isnan(b[inp.num_rows]))
+    rows = list(range(0, inp.num_rows, 7)) + [inp.num_rows - 1]
+    assert_logits_match(b[rows, : inp.width], oracle.paged_logits(inp, rows=rows), inp, rows, label=kind)
+
+
 def test_block_table_permutation_bitwise():
     inp = qsa_inputs.make_config("tiny")
     say("permutation")
