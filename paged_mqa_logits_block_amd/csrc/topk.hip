@@ -6,14 +6,17 @@
 // PR #48649, Accuracy Tests: rows that fit in k need no selection); nothing past n
 // is used (vLLM PR #62589, Details and Validation).
 //
-// One workgroup of 1024 threads (16 waves) per row.  The selection is reduced to
-// finding the k-th element in (value desc, column asc) order, a pair (T, Ct):
-// column c is kept iff key(c) > T, or key(c) == T and c <= Ct, where key is the
-// order-preserving u32 image of the float.
+// A row is selected by one workgroup of 1024 threads (16 waves); many-row calls
+// loop each workgroup over rows (topk_rows_kernel), few-row calls may share a
+// row among several workgroups (the split selection further down).  The
+// selection is reduced to finding the k-th element in (value desc, column asc)
+// order, a pair (T, Ct): column c is kept iff key(c) > T, or key(c) == T and
+// c <= Ct, where key is the order-preserving u32 image of the float.
 //
-// Rows of up to 32768 columns are staged once in LDS as keys (128 KB; every
-// global load of the row is in flight before the first is used); longer rows
-// are re-read from memory (L2) on every pass.
+// Rows of up to 32768 columns are held in registers (8 float4 per thread); a
+// finite row is selected from there with float compares (select_fast), any
+// other is staged once in LDS as keys (128 KB).  Longer rows are re-read from
+// memory (L2) on every pass.  The steps:
 //
 //  1. Finite min and max of the row (while staging; DPP wave reductions).
 //  2. A 2048-bucket histogram, buckets linear in value between min and max
@@ -421,12 +424,13 @@ struct RowRange {
 };
 
 template <class Sh>
-__device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite) {
-    const int w = threadIdx.x >> 6;
+__device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite,
+                                              int t = (int)threadIdx.x) {
+    const int w = t >> 6;
     kmax = wave_total_umax(kmax);
     const uint32_t nkmin = wave_total_umax(~kmin);
     nonfinite = wave_total_umax(nonfinite);
-    if ((threadIdx.x & 63) == 0) {
+    if ((t & 63) == 0) {
         sh.red_max[w] = kmax;
         sh.red_min[w] = nkmin;
         sh.red_nf[w] = nonfinite;
@@ -459,19 +463,15 @@ __device__ __forceinline__ void track(float x, bool valid, uint32_t &kmax, uint3
 // The whole selection of one row with n > k columns, by one workgroup.  STAGE:
 // rows of up to kStage columns are staged in LDS; without it (a lighter body
 // for a rare path) every row is re-read from memory on each pass.
-template <bool STAGE = true>
-__device__ __forceinline__ void select_full_row(Shared &sh, const float *src, int n, int k, int32_t *out) {
+// Steps 1-4 on a row of k < n <= kStage columns whose float4 groups are in
+// registers (x[j] = group t + kThreads*j; groups at or past (n+3)/4, and
+// columns past n, hold anything): keys staged to LDS, then the selection.
+__device__ __forceinline__ void select_staged(Shared &sh, const f32x4 (&x)[kStageGroups], int n, int k,
+                                              int32_t *out) {
     const int t = threadIdx.x;
     const int n4 = (n + 3) >> 2;
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nonfinite = 0u;
-    if (STAGE && n <= kStage) {
-        // ---- 1. stage the row: all loads in flight, then keys to LDS ------
-        f32x4 x[kStageGroups];
-#pragma unroll
-        for (int j = 0; j < kStageGroups; ++j) {
-            const int i = t + kThreads * j;
-            x[j] = (i < n4) ? load4(src, i) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    {
 #pragma unroll
         for (int j = 0; j < kStageGroups; ++j) {
             const int i = t + kThreads * j;
@@ -508,6 +508,23 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
             __syncthreads();
             select_row<kStageGroups>(sh, sk, n, k, bucket, out);
         }
+    }
+}
+
+template <bool STAGE = true>
+__device__ __forceinline__ void select_full_row(Shared &sh, const float *src, int n, int k, int32_t *out) {
+    const int t = threadIdx.x;
+    const int n4 = (n + 3) >> 2;
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nonfinite = 0u;
+    if (STAGE && n <= kStage) {
+        // ---- 1. stage the row: all loads in flight, then keys to LDS ------
+        f32x4 x[kStageGroups];
+#pragma unroll
+        for (int j = 0; j < kStageGroups; ++j) {
+            const int i = t + kThreads * j;
+            x[j] = (i < n4) ? load4(src, i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        select_staged(sh, x, n, k, out);
     } else {
         const StreamKeys sk{src, n};
 #pragma unroll 1
@@ -531,20 +548,283 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
     }
 }
 
-// ---- one workgroup per row --------------------------------------------------
+// ---- register-resident selection of a finite row ---------------------------
+//
+// The same selection as select_staged for the common case -- every visible
+// value finite, at most kCand values in the crossing bucket, and no tie at the
+// k-th value that the column order has to break among more than 64 members --
+// with the row kept in registers and compared as floats, so that each pass
+// costs a few vector operations per element:
+//  * range: NaN-propagating max3/min3 (a NaN or an infinity sends the row to
+//    select_staged);
+//  * buckets: floor(vmax*s - v*s) with one fma, clamped to [0, kBins-3], i.e.
+//    monotone non-increasing in v, the same expression in every pass;
+//  * the kept set: v > T or (v == T and column <= Ct), T as a float (for
+//    finite values the float order with +0 == -0 is the key order).
+// The kept columns are ranked in column order into LDS and written with
+// contiguous stores.  Returns false, having written nothing, in any other case.
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-    __shared__ Shared sh;
-    const int row = blockIdx.x;
-    const int t = threadIdx.x;
-    const int n = min(max(a.ctx_lens[row], 0), a.width);
-    const int k = a.k;
-    int32_t *out = a.idx_out + (int64_t)row * k;
-    if (n <= k) {  // the whole visible range is the selection
-        for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
-        return;
+__device__ __forceinline__ int fast_bucket(float v, float s, float off) {
+    return 1 + min((int)__builtin_fmaf(v, -s, off), kBins - 3);
+}
+
+__device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups], int n, int k, int32_t *out) {
+    int t = threadIdx.x;
+    // opaque to the optimiser: column indices derived from t are recomputed
+    // per row rather than kept live (in registers the row needs) across rows
+    asm volatile("" : "+v"(t));
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int n4 = (n + 3) >> 2;
+    // columns past n (in the last group, and in the copies of it that threads
+    // past the row loaded) take the value of the group's first column, which
+    // is visible: the range is unchanged, and every count below tests the
+    // column
+    const int tail = n - 4 * (n4 - 1);  // visible columns of the last group, 1..4
+    float mx = x[0][0], mn = x[0][0];
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+        const int i = t + kThreads * j;
+        if (i >= n4 - 1) {
+#pragma unroll
+            for (int e = 1; e < 4; ++e) x[j][e] = e < tail ? x[j][e] : x[j][0];
+        }
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(x[j][0], x[j][1]));
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(x[j][2], x[j][3]));
+        mn = __builtin_elementwise_minimum(mn, __builtin_elementwise_minimum(x[j][0], x[j][1]));
+        mn = __builtin_elementwise_minimum(mn, __builtin_elementwise_minimum(x[j][2], x[j][3]));
     }
-    select_full_row(sh, a.logits + (int64_t)row * a.stride, n, k, out);
+    const bool fin = __builtin_isfinite(mx) && __builtin_isfinite(mn);
+    const RowRange rr = row_range(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
+    if (!rr.all_finite) {
+        __syncthreads();
+        return false;
+    }
+    const float sc = rr.scale, off = rr.vmax * rr.scale;
+
+    // ---- histogram (cleared by row_range) --------------------------------
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+        const int i = t + kThreads * j;
+        if (4 * i + 4 <= n) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], sc, off)], 1u);
+        } else if (i < n4) {  // the last group: columns past n add 0
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], sc, off)], e < tail ? 1u : 0u);
+        }
+    }
+    __syncthreads();
+    find_crossing(sh, k);
+    const int bstar = sh.cross_bin;
+    int need = k - sh.cross_above;
+    int cnt = sh.cross_cnt;
+    if (cnt > kCand) {
+        __syncthreads();
+        return false;
+    }
+
+    // ---- the members of the crossing bucket, as (key, column) ------------
+    if (t == 0) sh.ncand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+        const int i = t + kThreads * j;
+        bool hit[4];
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hit[e] = (4 * i + e < n) & (fast_bucket(x[j][e], sc, off) == bstar);
+            any |= hit[e];
+        }
+        if (ballot(any)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint64_t m = ballot(hit[e]);
+                if (m) {
+                    const int lead = __builtin_ctzll(m);
+                    int base = 0;
+                    if (l == lead) base = atomicAdd(&sh.ncand, __popcll(m));
+                    base = readlane(base, lead);
+                    const int at = base + mask_prefix(m);
+                    if (hit[e]) {  // at < cnt <= kCand
+                        sh.cand_key[at] = order_key(x[j][e]);
+                        sh.cand_col[at] = 4 * i + e;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int nc = sh.ncand;  // == cnt: the same test as the histogram's
+
+    // ---- the k-th pair (T, Ct) -------------------------------------------
+    uint32_t T;
+    int tie_col;
+    if (nc <= 64) {
+        if (w == 0) {
+            const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
+            const int mc = l < nc ? sh.cand_col[l] : 0x7FFFFFFF;
+            int rank = 0;
+            for (int j = 0; j < nc; ++j) {
+                const uint32_t kj = (uint32_t)readlane((int)mk, j);
+                const int cj = readlane(mc, j);
+                rank += (kj > mk || (kj == mk && cj < mc)) ? 1 : 0;
+            }
+            if (l < nc && rank == need - 1) {
+                sh.thr_key = mk;
+                sh.tie_col = mc;
+            }
+        }
+        __syncthreads();
+        T = sh.thr_key;
+        tie_col = sh.tie_col;
+    } else {
+        radix_select(sh, [&](auto f) {
+            for (int j = t; j < nc; j += kThreads) f(sh.cand_key[j]);
+        }, T, need, cnt);
+        if (cnt > need) {  // the column order decides among equal values
+            __syncthreads();
+            return false;
+        }
+        tie_col = 0x7FFFFFFF;
+    }
+    const float Tf = key_value(T);
+
+    // ---- the kept set in column order, through LDS -----------------------
+    uint32_t sel = 0u;
+#pragma unroll
+    for (int j = 0; j < kStageGroups; ++j) {
+        const int c0 = 4 * (t + kThreads * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v = x[j][e];
+            const bool keep = (c0 + e < n) & ((v > Tf) | ((v == Tf) & (c0 + e <= tie_col)));
+            sel |= (keep ? 1u : 0u) << (4 * j + e);
+        }
+    }
+    static_assert(kStageGroups == kChunk, "one ranking round covers the row");
+    int offs[kChunk];
+    chunk_ranks(sh, sel, offs);
+    uint32_t *kept = sh.cand_key;  // k <= kCand column indices, in order (the members are no longer needed)
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+        int p = offs[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if ((sel >> (4 * j + e)) & 1u) {
+                if (p < k) kept[p] = (uint32_t)(4 * (t + kThreads * j) + e);
+                ++p;
+            }
+        }
+    }
+    __syncthreads();
+    for (int p = t; p < k; p += kThreads) out[p] = (int32_t)kept[p];
+    return true;
+}
+
+// Rows of a many-row call, round robin over a grid of workgroups that each take
+// at most kRowsPerGroup rows.  The next row that takes the register path is
+// copied into LDS (the staging area of the full selection, unused by
+// select_fast) by direct global-to-LDS loads while the current row is
+// selected, so its HBM reads overlap the selection and hold no registers.
+// These loads are issued from inline assembly: the compiler then neither
+// knows of them nor orders the selection's own LDS accesses behind them (it
+// would, for the builtin form, wait for every one before any LDS access); the
+// wait for them is explicit.  Rows the register path does not take (longer than
+// kStage, or refused by select_fast) are marked and selected after the loop by
+// the staged or streaming selection.
+constexpr int kRowsPerGroup = 2048;
+
+// 16 bytes per lane from global memory to LDS at lds_wave + 16 * lane (lds_wave
+// wave-uniform).  Leaves the load outstanding on the vector memory counter.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_wave) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_wave)
+        : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
+    __shared__ Shared sh;
+    __shared__ uint32_t later[kRowsPerGroup / 32];
+    const int t = threadIdx.x;
+    const int k = a.k;
+    const int stride = (int)gridDim.x;
+    f32x4 *pref = reinterpret_cast<f32x4 *>(sh.keys);  // the next row, group i at pref[i]
+    // read-only: through the constant address space its loads stay scalar
+    const __attribute__((address_space(4))) int32_t *ctx =
+        (const __attribute__((address_space(4))) int32_t *)a.ctx_lens;
+    auto visible = [&](int r) { return min(max(ctx[r], 0), a.width); };
+    auto fast_row = [&](int nn) { return k < nn && nn <= kStage; };
+    // every load at an in-row group (clamped)
+    auto prefetch = [&](int r, int nn) {
+        int tt = t;
+        asm volatile("" : "+v"(tt));  // addresses recomputed per row, not kept live across rows
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.logits + (int64_t)r * a.stride);
+        const int last = ((nn + 3) >> 2) - 1;
+        const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(uint32_t)(uintptr_t)(pref + (tt & ~63)));
+#pragma unroll
+        for (int j = 0; j < kStageGroups; ++j)
+            dma16(src + min(tt + kThreads * j, last), lds + 16u * kThreads * j);
+    };
+    for (int i = t; i < kRowsPerGroup / 32; i += kThreads) later[i] = 0u;
+    bool any_later = false;  // uniform
+    int rows_taken = 0;
+    int row = blockIdx.x;
+    int n = visible(row);
+    if (fast_row(n)) prefetch(row, n);
+    f32x4 x[kStageGroups];
+#pragma unroll 1
+    for (int m = 0;; ++m) {
+        const int nxt = row + stride;
+        const bool more = nxt < a.num_rows;
+        const int nn = more ? visible(nxt) : 0;
+        const bool fast = fast_row(n);
+        if (fast) {
+            wait_dma();
+            __syncthreads();
+            int tt = t;
+            asm volatile("" : "+v"(tt));
+#pragma unroll
+            for (int j = 0; j < kStageGroups; ++j) x[j] = pref[tt + kThreads * j];
+        }
+        __syncthreads();  // pref has been read (and the previous row is done with LDS)
+        if (more && fast_row(nn)) prefetch(nxt, nn);
+        int32_t *out = a.idx_out + (int64_t)row * k;
+        if (n <= k) {
+            for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
+        } else if (!fast || !select_fast(sh, x, n, k, out)) {
+            if (t == 0) later[m >> 5] |= 1u << (m & 31);
+            any_later = true;
+        }
+        rows_taken = m + 1;
+        if (!more) break;
+        row = nxt;
+        n = nn;
+    }
+    if (!any_later) return;
+    __syncthreads();
+#pragma unroll 1
+    for (int wd = 0; wd < (rows_taken + 31) >> 5; ++wd) {
+        uint32_t bits = later[wd];
+        while (bits) {
+            const int m = 32 * wd + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int r = (int)blockIdx.x + m * stride;
+            select_full_row<false>(sh, a.logits + (int64_t)r * a.stride, visible(r), k, a.idx_out + (int64_t)r * k);
+            __syncthreads();
+        }
+    }
 }
 
 // ---- split selection: several workgroups per row ----------------------------
@@ -586,6 +866,7 @@ constexpr int kSlotLoads = 8;         // member slots a resolve thread loads
 constexpr int kHistLoads = 5;         // histogram words a resolve thread loads (17 slices)
 constexpr int kSplitCUs = 256;        // workgroups that fill the chip once
 constexpr int kSplitMaxRows = kSplitCUs / 2;
+constexpr int kRowsGrid = 256;         // one workgroup per CU (LDS)
 
 struct WindowShared {
     alignas(16) uint32_t hist[kBins];
@@ -1060,7 +1341,10 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEv
             default: return hipErrorInvalidValue;
         }
     } else {
-        hipExtLaunchKernelGGL(topk_kernel, dim3((unsigned)a.num_rows), dim3(kThreads), 0, s, start, stop, 0, a);
+        // one workgroup per CU, more when a workgroup would take over kRowsPerGroup rows
+        unsigned g = (unsigned)(a.num_rows < kRowsGrid ? a.num_rows : kRowsGrid);
+        g = g > (unsigned)((a.num_rows + kRowsPerGroup - 1) / kRowsPerGroup) ? g : (unsigned)((a.num_rows + kRowsPerGroup - 1) / kRowsPerGroup);
+        hipExtLaunchKernelGGL(topk_rows_kernel, dim3(g), dim3(kThreads), 0, s, start, stop, 0, a);
     }
     return hipGetLastError();
 }

@@ -437,6 +437,31 @@ def test_topk_rows_shared_or_not(rows, W, k):
     assert_topk_exact(g1, oi, label=f"rows {rows} one workgroup per row")
 
 
+@pytest.mark.parametrize("rows", [300, 600])
+def test_topk_many_rows_infinities_and_fallbacks(rows):
+    """Many rows per workgroup (rows > 256): finite rows take the register
+    path; rows with +inf / -inf inside the visible range, one-value rows and
+    rows of small integers (tie groups larger than the LDS list) are set aside
+    and selected after the others; every row equals the oracle."""
+    W, k = 9000, 2048
+    rng = np.random.default_rng(rows)
+    ctx = rng.integers(k - 50, W + 1, size=rows)
+    ctx[::7] = W - 1  # a partial last float4 group
+    kinds = ["normal", "relu", "ints", "const", "normal", "zeros"]
+    x = np.concatenate([qsa_inputs.make_logits(1, W, [int(ctx[r])], seed=r, kind=kinds[r % 6])
+                        for r in range(rows)])
+    for r in range(0, rows, 11):
+        n = int(ctx[r])
+        cols = rng.integers(0, n, size=5)
+        x[r, cols[:3]] = np.inf
+        x[r, cols[3:]] = -np.inf
+    say("topk many rows inf", rows)
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    g = gpu_topk(xt, ct, k, workspace=None).cpu().numpy()
+    assert_topk_exact(g, oracle.topk(x, ctx, k), label=f"many rows inf {rows}")
+
+
 def test_topk_sample_miss_falls_back():
     """Rows whose sampled columns are far below (or above) the rest: the
     sample's window misses the k-th value and the row takes the histogram
