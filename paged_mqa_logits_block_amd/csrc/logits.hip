@@ -583,7 +583,7 @@ constexpr int kMtpDepth = 4;                  // runs in flight
 constexpr int kMtpMaxRuns = kMtpMaxRunsPerGroup;  // runs per workgroup at most
 
 template <int H, bool HAS_W, bool HAS_SCALE>
-__global__ __launch_bounds__(256) void mtp_fp8_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
     typedef Frag<true> F;
     constexpr int MT = H / 16;
     constexpr int D = kMtpDepth;
@@ -697,7 +697,9 @@ __global__ __launch_bounds__(256) void mtp_fp8_kernel(LogitsArgs a) {
             };
             // scores of run j (in LDS buffer buf) into obuf
             auto score = [&](int j, int buf) {
-                const bool ok = __builtin_amdgcn_readfirstlane(okbuf[buf]) != 0;
+                // lane 16 g + i: this lane group's heads summed for column
+                // 16 tt + i of each tile tt
+                float part[4];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const typename F::T b =
@@ -708,16 +710,29 @@ __global__ __launch_bounds__(256) void mtp_fp8_kernel(LogitsArgs a) {
                     f32x4 acc[MT];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) acc[mt] = F::mma(qa[mt], b, f32x4{0.f, 0.f, 0.f, 0.f});
-                    float val = 0.0f;
+                    float v = 0.0f;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) val += wv[mt][i] * relu(acc[mt][i]);
-                    val = xor32_sum(xor16_sum(val));
-                    const float sc = HAS_SCALE ? sbuf[buf][16 * tt + (l & 15)] : 1.0f;
-                    // every lane group holds the sum: all write, equal values
-                    obuf[w][kMtpRun * j + 16 * tt + (l & 15)] = ok ? val * sc : qnan;
+                        for (int i = 0; i < 4; ++i) v += wv[mt][i] * relu(acc[mt][i]);
+                    part[tt] = v;
                 }
+                // sum over the 4 lane groups, scattered so that lane l ends
+                // with column l: exchanging the halves (tiles 0/2 and 1/3)
+                // leaves tiles 0, 1 summed over groups {g, g^2} in the lower
+                // half and tiles 2, 3 in the upper; exchanging odd and even
+                // 16-lane rows then leaves tile g in group g
+                const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]),
+                                                                  false, false);
+                const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]),
+                                                                  false, false);
+                const float r0 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
+                const float r1 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
+                const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(r0), __float_as_uint(r1), false, false);
+                const float val = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+                const bool ok = __builtin_amdgcn_readfirstlane(okbuf[buf]) != 0;
+                const float sc = HAS_SCALE ? sbuf[buf][l] : 1.0f;
+                obuf[w][kMtpRun * j + l] = ok ? val * sc : qnan;
             };
 
             i32x8 kring[D];
