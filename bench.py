@@ -35,8 +35,12 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per paged MQA-logits+top-k call; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_logits_block_amd", "csrc", f)
-                  for f in ("logits.hip", "qsa_device.h", "qsa_internal.h")]
+CSRC = os.path.join(ROOT, "paged_mqa_logits_block_amd", "csrc")
+# each scoring kernel's own source file; the planner and the shared headers
+# are part of every kernel's hash
+KERNEL_FILES = {"paged_logits_kernel": "logits_decode.hip", "looped_logits_kernel": "logits_looped.hip",
+                "mtp_fp8_kernel": "logits_mtp.hip", "prefill_logits_kernel": "logits_prefill.hip"}
+COMMON_SOURCES = ("logits.hip", "logits_frag.h", "qsa_device.h", "qsa_internal.h")
 
 DESCRIPTIONS = {
     "tiny": "2 requests x 4 rows, 4 heads, D=128, bf16, ctx 1000/3000, block 16, top-k 256",
@@ -87,26 +91,82 @@ def scoring_kernel(inp):
     return "paged_logits_kernel"
 
 
-def source_hash():
+def source_hash(kernel):
+    """Hash of the sources a scoring kernel is built from."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in (KERNEL_FILES[kernel], *COMMON_SOURCES):
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    once the kernel sources differ from the ones the counters were taken on."""
+    once the kernel's sources differ from the ones the counters were taken on."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
+
+
+def _counter_rows(folder, counter):
+    """(kernel name, value) per dispatch from rocprofv3 counter-collection CSVs
+    under `folder`."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def write_traffic(workload, kernel, dirs, calib_mib):
+    """Record the scoring kernel's HBM bytes per launch in profiles/traffic.json.
+
+    dirs = (FETCH_SIZE run, WRITE_SIZE run, FETCH_SIZE run of the calibration
+    copy, WRITE_SIZE run of the calibration copy): rocprofv3 output folders.
+    Both counters read KiB per dispatch; each is scaled by what it reads for a
+    plain device copy of calib_mib MiB each way (the copy's largest dispatch)."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    copy_kib = calib_mib * 1024.0
+    out = {}
+    for name, d, cd in (("fetch", fetch_dir, cfetch_dir), ("write", write_dir, cwrite_dir)):
+        counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
+        scale = copy_kib / max(v for _, v in _counter_rows(cd, counter))
+        vals = [(k, v) for k, v in _counter_rows(d, counter) if kernel in k]
+        if not vals:
+            raise SystemExit(f"no {kernel} dispatches with {counter} under {d}")
+        out[name] = (statistics.mean(v for _, v in vals) * 1024.0 * scale, scale, len(vals), vals[0][0])
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    full_name = out["fetch"][3].removeprefix("void ")
+    table[workload] = {
+        "source_hash": source_hash(kernel),
+        "kernel": full_name[:full_name.rindex("(")] if full_name.endswith(")") else full_name,
+        "fetch_bytes": round(out["fetch"][0]),
+        "write_bytes": round(out["write"][0]),
+        "bytes_per_launch": round(out["fetch"][0] + out["write"][0]),
+        "fetch_scale": round(out["fetch"][1], 4),
+        "write_scale": round(out["write"][1], 4),
+        "dispatches": out["fetch"][2],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: table[workload]}))
 
 
 def cpu_baseline(inp, budget_s=20.0):
@@ -140,6 +200,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_verify", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_FETCH_DIR",
+                                                          "CALIB_WRITE_DIR"),
+                    help="record the scoring kernel's counter bytes from rocprofv3 --pmc output "
+                         "folders (FETCH_SIZE, WRITE_SIZE, and both for a --calib-copy-mib run); "
+                         "no GPU needed")
+    ap.add_argument("--calib-mib", type=int, default=1024, help="size of the calibration copy")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -148,6 +214,12 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the scoring path has no multi-GPU variant in this library)", file=sys.stderr)
         sys.exit(2)
+
+    if args.write_traffic:
+        import qsa_inputs
+        inp = qsa_inputs.make_config(args.workload)
+        write_traffic(args.workload, scoring_kernel(inp), args.write_traffic, args.calib_mib)
+        return
 
     import numpy as np
     import torch
@@ -223,7 +295,7 @@ def main():
     topk_us = statistics.mean(e[2].elapsed_time(e[3]) for e in evs) * 1e3
 
     achieved = per_call / (logit_us * 1e-6) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, scoring_kernel(inp))
     line = {
         "metric": METRIC,
         "value": round(us_per_call, 2),

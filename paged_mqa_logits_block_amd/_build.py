@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqsaidx.so")
-SOURCES = ["api.hip", "logits.hip", "topk.hip"]
+SOURCES = ["api.hip", "logits.hip", "logits_decode.hip", "logits_looped.hip", "logits_mtp.hip",
+           "logits_prefill.hip", "topk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -29,10 +30,7 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB, extra=None, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,6 +40,24 @@ def build(out: str = LIB, extra=None, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(out: str = LIB, extra=None, verbose: bool = False) -> str:
+    """Compile every source to an object in a temporary folder (in parallel),
+    link the shared library next to `out` and move it into place."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    flags = [*FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC]
+    compile_flags = [f for f in flags if f != "-shared"]
+    tmp = out + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="qsaidx_build_") as objdir:
+        objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *compile_flags, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
     return out
 

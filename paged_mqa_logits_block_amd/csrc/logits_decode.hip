@@ -1,0 +1,296 @@
+// Paged MQA-logits scoring on gfx950: stacked-M MFMA kernel.
+//
+// Method (ROCm/ATOM PR #2651, "Changes"): the rows x heads that share a
+// request's keys form the M operand of one matrix multiply, so a key tile is
+// read from HBM once per request instead of once per row; the per-head ReLU is
+// applied to the accumulator before the heads are summed back out of M.  Key
+// columns are gathered through the block table (ROCm/aiter PR #4221, block-flat
+// commit: block kv_indices[b, col // KVB], slot col % KVB).  Programs whose
+// column chunk lies past every row's visible count only write -inf (vLLM
+// PR #62589, "Overview" and "Details"; sglang PR #48649, "Modifications").
+//
+// Layout of the work:
+//  * one program = one wave64 = (row tile, column chunk); a row tile is RT rows
+//    whose RT*H (row, head) pairs fill MT stacked 16-row MFMA tiles;
+//  * a column chunk is TPW tiles of 16 key columns; B % 16 == 0 so a tile never
+//    straddles a pool block and costs one table lookup (a scalar load);
+//  * the key tile is loaded straight from the pool into the MFMA B operand:
+//    lane l reads key column (l % 16), 16 contiguous bytes per K step, so each
+//    load instruction moves 16 rows x 64 contiguous bytes;
+//  * Q (the A operand) stays in registers for the whole program;
+//  * accumulator lane l holds M rows 4*(l/16)..+3 of column l % 16; with
+//    m = row*H + head, the head sum is in-lane for H <= 4, plus one or two
+//    cross-lane steps for H >= 8.
+#include "logits_frag.h"
+
+namespace qsa {
+namespace {
+
+// H heads, MT stacked 16-row tiles, TPW 16-column tiles per program.
+template <bool FP8, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE>
+__global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
+    typedef Frag<FP8> F;
+    constexpr int M = 16 * MT;
+    static_assert(M % H == 0, "a row's heads must fit in the stacked tiles");
+    constexpr int RT = M / H;  // rows per tile
+    static_assert(RT >= 1 && RT <= 16, "row info is held by lanes 0..15");
+    // After the head reduction a lane stores NR rows: for H <= 4 the 4/H rows
+    // whose heads sit in its own 4 accumulator slots; for H >= 8 one row per
+    // stacked tile group (the lane group that owns it stores it).
+    constexpr int NR = (H <= 4) ? 4 / H : RT;
+
+    const int l = lane_id();
+    const int g = l >> 4;  // lane group
+    const int tile = blockIdx.x / a.num_chunks;
+    const int chunk = blockIdx.x - tile * a.num_chunks;
+    const int row0 = tile * RT;
+    const int c0 = chunk * TPW * 16;
+
+    // per-row info of the tile, wave-uniform: every load issued before any use
+    // (indices clamped in bounds, padding rows masked afterwards)
+    int ctx_r[RT], req_r[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int row = min(row0 + r, a.num_rows - 1);
+        ctx_r[r] = a.ctx_lens[row];
+        req_r[r] = a.row_to_req[row];
+    }
+    uint32_t todo = 0u;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const bool valid = row0 + r < a.num_rows;
+        ctx_r[r] = valid ? min(max(ctx_r[r], 0), a.cap) : 0;
+        req_r[r] = valid ? req_r[r] : -1;
+        todo |= (valid ? 1u : 0u) << r;
+    }
+
+    // resident Q: the A operand of every stacked tile and K step;
+    // stacked row m = 16*mt + (l % 16) is (tile row m / H, head m % H)
+    typename F::T qa[MT][F::kSteps];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + (l & 15);
+        const int row = row0 + m / H, h = m % H;
+        const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) +
+                              ((int64_t)row * H + h) * F::kRowBytes + F::lane_bytes(l);
+#pragma unroll
+        for (int s = 0; s < F::kSteps; ++s)
+            qa[mt][s] = (row < a.num_rows) ? F::load(qrow, s) : F::zero();
+    }
+
+    // weights of the accumulator slots this lane holds: slot (mt, i) is stacked
+    // row m = 16*mt + 4*g + i
+    float wv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * mt + 4 * g + i;
+            const int row = row0 + m / H, h = m % H;
+            wv[mt][i] = (HAS_W && row < a.num_rows) ? a.w[(int64_t)row * H + h] : 1.0f;
+        }
+
+    // tile row of the j-th row this lane stores, and whether this lane stores it
+    int st_rr[NR];
+    bool st_lane[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        if (H <= 4) {
+            st_rr[j] = (4 * g + j * H) / H;
+            st_lane[j] = true;
+        } else {
+            // row j occupies stacked rows j*H .. j*H+H-1, i.e. lane groups
+            // (j*H/4) % 4 .. ; the lowest of them stores it
+            st_rr[j] = j;
+            st_lane[j] = (H >= 16) ? (g == 0) : (g == (j * H / 4) % 4);
+        }
+    }
+
+    const float neg_inf = -__builtin_inff();
+    const float qnan = __builtin_nanf("");
+
+    while (todo) {
+        // the rows of one request: the lowest pending row's request
+        const int r0 = __builtin_ctz(todo);
+        int req = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) req = (r == r0) ? req_r[r] : req;
+        uint32_t set = 0u;
+        int vis = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (((todo >> r) & 1u) && req_r[r] == req) {
+                set |= 1u << r;
+                vis = max(vis, ctx_r[r]);
+            }
+        }
+        todo &= ~set;
+        // a row_to_req value outside the table is never dereferenced: its rows
+        // read no keys and their visible columns are written as NaN
+        const bool req_ok = req >= 0 && req < a.num_reqs;
+        const int32_t *bt = a.block_table + (req_ok ? (int64_t)req * a.max_blocks : 0);
+
+        // per stored row: its visible count, and whether this request owns it
+        int st_ctx[NR];
+        bool st_on[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            int c = 0;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) c = (st_rr[j] == r) ? ctx_r[r] : c;
+            st_ctx[j] = c;
+            st_on[j] = st_lane[j] && ((set >> st_rr[j]) & 1u);
+        }
+
+        // Keys of the chunk: all table entries, then all key tiles, issued
+        // before the first is used.  A tile that is past the visible range or
+        // whose table entry is out of range loads block 0 (always in the pool)
+        // and its scores are discarded.  A chunk entirely past the visible
+        // range loads nothing.
+        const bool any_live = c0 < vis;
+        typename F::T b[TPW][F::kSteps];
+        float kscale[TPW];
+        bool ok[TPW];
+        if (any_live) {
+            int blk[TPW], slot0[TPW];
+            ColCursor cur(c0, a.block_size);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                blk[t] = req_ok ? bt[min(cur.q, a.max_blocks - 1)] : -1;
+                slot0[t] = cur.r;
+                cur.step(a.block_size);
+            }
+            // per lane: key column l % 16 of the tile, its slice of the row
+            const int lane_key = (l & 15) * (int)a.key_stride + F::lane_bytes(l);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int col0 = c0 + 16 * t;
+                ok[t] = col0 < vis && blk[t] >= 0 && (int64_t)blk[t] < a.num_blocks;
+                // wave-uniform tile base (block 0 when the tile is not scored)
+                const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
+                const int tslot = ok[t] ? slot0[t] : 0;
+                const uint8_t *kt = a.kcache + bbase + (int64_t)tslot * a.key_stride;
+#pragma unroll
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kt + lane_key, s);
+                kscale[t] = 1.0f;
+                if (HAS_SCALE) {
+                    if (a.layout == 1)
+                        kscale[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
+                    else
+                        kscale[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                ok[t] = false;
+                kscale[t] = 1.0f;
+#pragma unroll
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::zero();
+            }
+        }
+
+        // Scores of every tile first, stores after: on gfx9 the memory counter
+        // that orders a wait on loaded data also covers earlier stores, so a
+        // store between two tiles would hold the next tile until it lands.
+        float val[TPW][NR];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f32x4 acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s = 0; s < F::kSteps; ++s) acc[mt] = F::mma(qa[mt][s], b[t][s], acc[mt]);
+
+            // head reduction: per stored row, sum of w * ReLU over its heads
+            if (H <= 4) {
+#pragma unroll
+                for (int j = 0; j < NR; ++j) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int i = j * H; i < j * H + H; ++i) v += wv[0][i] * relu(acc[0][i]);
+                    val[t][j] = v;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NR; ++j) val[t][j] = 0.0f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    // all 4 slots of tile mt belong to tile row (16*mt + 4*g) / H
+                    // (16*mt / H for H >= 16: known at compile time)
+                    const int rr = H >= 16 ? (16 * mt) / H : (16 * mt + 4 * g) / H;
+                    float c = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) c += wv[mt][i] * relu(acc[mt][i]);
+#pragma unroll
+                    for (int j = 0; j < NR; ++j)
+                        if (j == rr) val[t][j] += c;
+                }
+#pragma unroll
+                for (int j = 0; j < NR; ++j) {
+                    if (H >= 8) val[t][j] = xor16_sum(val[t][j]);
+                    if (H >= 16) val[t][j] = xor32_sum(val[t][j]);
+                }
+            }
+        }
+
+        // mask and store: lane writes column col0 + l%16 of each row it stores
+        float *orow[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) orow[j] = a.out + (int64_t)(row0 + st_rr[j]) * a.out_stride + c0;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int col0 = c0 + 16 * t;
+            const bool live = col0 < vis;
+            const int cc = 16 * t + (l & 15);  // column - c0
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                if (st_on[j] && c0 + cc < a.width) {
+                    const float v = live ? (ok[t] ? val[t][j] * kscale[t] : qnan) : neg_inf;
+                    orow[j][cc] = c0 + cc < st_ctx[j] ? v : neg_inf;
+                }
+            }
+        }
+    }
+}
+
+template <bool FP8, int H, int MT, int TPW>
+hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
+    const bool has_w = a.w != nullptr;
+    const bool has_s = FP8 && (a.layout == 1 || a.kscale != nullptr);
+    if (has_w && has_s)
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, true>), grid, block, 0, s, e0, e1, 0, a);
+    else if (has_w)
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, false>), grid, block, 0, s, e0, e1, 0, a);
+    else if (has_s)
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, true>), grid, block, 0, s, e0, e1, 0, a);
+    else
+        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, false>), grid, block, 0, s, e0, e1, 0, a);
+    return hipGetLastError();
+}
+
+// (stacked tiles, tiles per program) by head count, as plan_logits chooses them
+template <bool FP8>
+hipError_t launch_heads(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    switch (a.num_heads) {
+        case 1: return launch_h<FP8, 1, 1, 4>(a, s, e0, e1);
+        case 2: return launch_h<FP8, 2, 1, 4>(a, s, e0, e1);
+        case 4: return launch_h<FP8, 4, 1, 4>(a, s, e0, e1);
+        case 8: return launch_h<FP8, 8, 1, 8>(a, s, e0, e1);
+        case 16: return launch_h<FP8, 16, 1, 8>(a, s, e0, e1);
+        case 32: return launch_h<FP8, 32, 2, 8>(a, s, e0, e1);
+        case 64: return launch_h<FP8, 64, 4, 8>(a, s, e0, e1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    return a.dtype == 0 ? launch_heads<false>(a, s, e0, e1) : launch_heads<true>(a, s, e0, e1);
+}
+
+}  // namespace qsa
