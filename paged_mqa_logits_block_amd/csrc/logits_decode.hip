@@ -71,6 +71,25 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         ctx_r[r] = a.ctx_lens[row];
         req_r[r] = a.row_to_req[row];
     }
+    // The table entries of the chunk for a guessed request, loaded in the same
+    // round trip as the row info: request-major rows, the same count per
+    // request (every decode batch here) make the guess exact; a wrong guess
+    // only costs a second round of table loads below.
+    // Only for 4 or fewer heads: with more, most programs of the long mixed
+    // single-row batch lie past their row's context and the guessed loads
+    // are wasted there.
+    constexpr bool GUESS = H <= 4;
+    const int guess = GUESS ? min((int)(((int64_t)row0 * a.num_reqs) / a.num_rows), a.num_reqs - 1) : -1;
+    int gblk[TPW];
+    if constexpr (GUESS) {
+        const int32_t *gbt = a.block_table + (int64_t)guess * a.max_blocks;
+        ColCursor cur(c0, a.block_size);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            gblk[t] = gbt[min(cur.q, a.max_blocks - 1)];
+            cur.step(a.block_size);
+        }
+    }
     uint32_t todo = 0u;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -168,11 +187,20 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         if (any_live) {
             int blk[TPW], slot0[TPW];
             ColCursor cur(c0, a.block_size);
+            if (GUESS && req == guess) {
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                blk[t] = req_ok ? bt[min(cur.q, a.max_blocks - 1)] : -1;
-                slot0[t] = cur.r;
-                cur.step(a.block_size);
+                for (int t = 0; t < TPW; ++t) {
+                    blk[t] = gblk[t];
+                    slot0[t] = cur.r;
+                    cur.step(a.block_size);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    blk[t] = req_ok ? bt[min(cur.q, a.max_blocks - 1)] : -1;
+                    slot0[t] = cur.r;
+                    cur.step(a.block_size);
+                }
             }
             // per lane: key column l % 16 of the tile, its slice of the row
             const int lane_key = (l & 15) * (int)a.key_stride + F::lane_bytes(l);
