@@ -52,6 +52,10 @@ DESCRIPTIONS = {
                  "w U(0,1), kv_len 32768, co-packed KVB=64, top-k 2048",
     "prefill_chunk": "1 request, 16384 rows at positions 98304..114687, 4 heads, D=128, bf16, "
                      "ctx (pos+1)//4, block 64, top-k 2048",
+    "decode_verify_fp16": "decode_verify with fp16 q/k: 9 requests x 4 MTP rows, 4 heads, D=128, "
+                          "ctx U[16000,32000], block 16, top-k 2048",
+    "prefill_chunk_fp16": "prefill_chunk with fp16 q/k: 1 request, 16384 rows, 4 heads, D=128, "
+                          "ctx (pos+1)//4, block 64, top-k 2048",
 }
 
 
@@ -75,12 +79,12 @@ def algorithmic_bytes(inp):
 
 def scoring_kernel(inp):
     """The scoring kernel the library picks for this shape (the same rule as
-    its planner): the prefill variant for bf16, 4 heads and one request with
+    its planner): the prefill variant for bf16 or fp16, 4 heads and one request with
     256+ rows and blocks of a multiple of 32 columns; the 4-row variant for fp8
     with 32/64 heads, 4 rows per request and blocks of a multiple of 64
     columns; the looped variant for other fp8 shapes with 16+ heads; the
     per-tile variant otherwise."""
-    if (inp.dtype == "bf16" and inp.num_heads == 4 and inp.num_reqs == 1 and inp.num_rows >= 256
+    if (inp.dtype in ("bf16", "fp16") and inp.num_heads == 4 and inp.num_reqs == 1 and inp.num_rows >= 256
             and inp.block_size % 32 == 0):
         return "prefill_logits_kernel"
     if (inp.dtype == "fp8" and inp.num_heads in (32, 64) and inp.num_rows == 4 * inp.num_reqs

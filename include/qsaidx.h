@@ -59,7 +59,9 @@ typedef enum qsa_status {
 
 typedef enum qsa_dtype {
     QSA_BF16 = 0,          /* bfloat16 q and keys                                   */
-    QSA_FP8_E4M3FN = 1     /* OCP fp8 E4M3 ("fn": no infinities, max 448) q and keys */
+    QSA_FP8_E4M3FN = 1,    /* OCP fp8 E4M3 ("fn": no infinities, max 448) q and keys */
+    QSA_FP16 = 2           /* IEEE binary16 q and keys (vLLM #62589, "Details": the  */
+                           /* dot runs in fp16 for fp16 inputs, fp32 accumulation)   */
 } qsa_dtype;
 
 typedef enum qsa_kv_layout {
@@ -96,7 +98,7 @@ typedef struct qsa_logits_shape {
  *   w           [R][H] f32, or NULL for w = 1.
  *   kcache      key pool in kv_layout (see qsa_kv_layout).
  *   kscale      QSA_KV_PAGED + fp8: [num_blocks][B] f32 or NULL (scale 1).
- *               Must be NULL for bf16 and for QSA_KV_COPACKED.
+ *               Must be NULL for bf16, fp16 and QSA_KV_COPACKED.
  *   block_table [num_reqs][max_blocks] int32 pool block indices.
  *   ctx_lens    [R] int32 visible columns per row.
  *   row_to_req  [R] int32 row -> block_table row.
@@ -113,7 +115,8 @@ typedef struct qsa_logits_shape {
  * columns of every tile it would feed NaN.
  *
  * Compiled set (else QSA_E_UNSUPPORTED): D = 128; H in {1,2,4,8,16,32,64};
- * B a multiple of 16 in [16, 1024]; bf16 + PAGED, fp8 + PAGED, fp8 + COPACKED.
+ * B a multiple of 16 in [16, 1024]; bf16 + PAGED, fp16 + PAGED, fp8 + PAGED,
+ * fp8 + COPACKED.
  * Alignment (else QSA_E_ALIGN): q, kcache, out 16-byte aligned; out_stride % 4 == 0.
  * Range (else QSA_E_RANGE): W <= 1<<24; R*out_stride*4 and num_blocks*block
  * bytes below 2^62.

@@ -48,6 +48,8 @@ def load(path: Optional[str] = None):
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.ora_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.ora_bf16_to_double.restype = ctypes.c_double
+    lib.ora_fp16_to_double.argtypes = [ctypes.c_uint16]
+    lib.ora_fp16_to_double.restype = ctypes.c_double
     lib.ora_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
     lib.ora_e4m3fn_to_double.restype = ctypes.c_double
     lib.ora_paged_logits.argtypes = [
@@ -79,6 +81,7 @@ class OracleError(RuntimeError):
 
 
 _GUARD = 64
+_DTYPE_CODES = {"bf16": 0, "fp8": 1, "fp16": 2}
 _SENTINEL = 1.2345e300
 
 
@@ -86,6 +89,12 @@ def decode_bf16(bits) -> np.ndarray:
     lib = load()
     b = np.asarray(bits, dtype=np.uint16)
     return np.array([lib.ora_bf16_to_double(int(v)) for v in b.ravel()]).reshape(b.shape)
+
+
+def decode_fp16(bits) -> np.ndarray:
+    lib = load()
+    b = np.asarray(bits, dtype=np.uint16)
+    return np.array([lib.ora_fp16_to_double(int(v)) for v in b.ravel()]).reshape(b.shape)
 
 
 def decode_e4m3fn(codes) -> np.ndarray:
@@ -112,7 +121,7 @@ def paged_logits(inp, rows: Optional[Sequence[int]] = None, threads: int = 0,
     buf[n * inp.width:] = _SENTINEL
     out = buf[: n * inp.width].reshape(n, inp.width)
     st = lib.ora_paged_logits(
-        _ptr(q), 0 if inp.dtype == "bf16" else 1, _ptr(w), _ptr(kc),
+        _ptr(q), _DTYPE_CODES[inp.dtype], _ptr(w), _ptr(kc),
         0 if inp.layout == "paged" else 1, _ptr(ks), _i32(bt), _i32(ctx), _i32(r2r),
         inp.num_rows, inp.num_heads, inp.head_dim, inp.block_size, inp.num_reqs,
         inp.max_blocks, inp.num_blocks, inp.width, _ptr(sel), n, _ptr(out), threads)

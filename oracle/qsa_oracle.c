@@ -6,7 +6,7 @@
  * check and the benchmark's CPU-baseline leg load it; the product path never
  * does.  It shares no source, header or helper with the HIP library.
  *
- * Arithmetic is float64 (inputs are bf16 / fp8 / f32, all exact in float64),
+ * Arithmetic is float64 (inputs are bf16 / fp16 / fp8 / f32, all exact in float64),
  * loops run in the order the definition is written, and the file is compiled
  * with -O2 -ffp-contract=off and without -ffast-math.  OpenMP only splits rows
  * across threads; each output is computed by one thread in a fixed order.
@@ -22,10 +22,11 @@
  *    that extends the fp8 paged kernel to any block size); the -inf mask is
  *    compared exactly by its test gate.
  *  - vLLM PR #62589, "Overview"/"Details": columns past a row's visible count
- *    are masked; "Validation": top-k reads only [0, visible), compared as sets.
+ *    are masked; "Validation": top-k reads only [0, visible), compared as sets;
+ *    "Details": fp16 q and keys are scored as fp16 (dtype code 2 here).
  *
  * Pins (tests/test_oracle_pins.py) tie every function here to something other
- * than itself: library fp8/bf16 conversions, one-hot closed forms, GEMV special
+ * than itself: library fp8/bf16/fp16 conversions, one-hot closed forms, GEMV special
  * cases, invariants (zero heads, permutation, scale powers of two), and brute
  * force over all subsets for the selection.
  */
@@ -49,6 +50,33 @@ double ora_bf16_to_double(uint16_t bits)
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/*
+ * IEEE 754 binary16: 1 sign bit, 5 exponent bits with bias 15, 10 mantissa
+ * bits; exponent field 0 encodes subnormals m/1024 * 2^-14; exponent field 31
+ * is infinity (m = 0) or NaN.  Every binary16 value is exact in float64.
+ */
+double ora_fp16_to_double(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 10) & 0x1F;
+    int m = bits & 0x3FF;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m / 1024.0, -14);
+    else
+        v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
+/* element `at` of a bf16 (dtype 0) or fp16 (dtype 2) array, as float64 */
+static double half_elem(const void *p, int dtype, int64_t at)
+{
+    uint16_t b = ((const uint16_t *)p)[at];
+    return dtype == 0 ? ora_bf16_to_double(b) : ora_fp16_to_double(b);
 }
 
 /*
@@ -83,11 +111,10 @@ static int fetch_key(double *kd, int dtype, int layout, const void *kcache, cons
     int slot = col % block_size;
     if (blk < 0 || (int64_t)blk >= num_blocks)
         return ORA_E_TABLE;
-    if (dtype == 0) {
-        const uint16_t *k = (const uint16_t *)kcache +
-                            ((int64_t)blk * block_size + slot) * head_dim;
+    if (dtype == 0 || dtype == 2) {
+        int64_t base = ((int64_t)blk * block_size + slot) * head_dim;
         for (int d = 0; d < head_dim; ++d)
-            kd[d] = ora_bf16_to_double(k[d]);
+            kd[d] = half_elem(kcache, dtype, base + d);
         return ORA_OK;
     }
     const uint8_t *k;
@@ -131,9 +158,9 @@ int ora_paged_logits(const void *q, int dtype, const float *w, const void *kcach
     if (num_rows < 0 || num_heads < 1 || head_dim < 1 || block_size < 1 || num_reqs < 1 ||
         max_blocks < 1 || num_blocks < 1 || width < 0 || n_rows < 0)
         return ORA_E_ARG;
-    if (dtype != 0 && dtype != 1)
+    if (dtype != 0 && dtype != 1 && dtype != 2)
         return ORA_E_ARG;
-    if (dtype == 0 && layout != 0)
+    if (dtype != 1 && layout != 0)
         return ORA_E_ARG;
     if (!rows)
         n_rows = num_rows;
@@ -174,9 +201,8 @@ int ora_paged_logits(const void *q, int dtype, const float *w, const void *kcach
         for (int h = 0; h < num_heads; ++h)
             for (int d = 0; d < head_dim; ++d) {
                 int64_t at = ((int64_t)row * num_heads + h) * head_dim + d;
-                qd[h * head_dim + d] = dtype == 0
-                                           ? ora_bf16_to_double(((const uint16_t *)q)[at])
-                                           : ora_e4m3fn_to_double(((const uint8_t *)q)[at]);
+                qd[h * head_dim + d] = dtype == 1 ? ora_e4m3fn_to_double(((const uint8_t *)q)[at])
+                                                  : half_elem(q, dtype, at);
             }
         for (int64_t col = 0; col < ctx; ++col) {
             if (fetch_key(kd, dtype, layout, kcache, kscale, block_table, max_blocks, num_blocks,

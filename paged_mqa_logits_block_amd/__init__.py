@@ -21,7 +21,7 @@ OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_RANGE, E_ALIGN, E_HIP = range(7)
 STATUS_NAMES = {0: "QSA_OK", 1: "QSA_E_INVALID", 2: "QSA_E_DTYPE", 3: "QSA_E_UNSUPPORTED",
                 4: "QSA_E_RANGE", 5: "QSA_E_ALIGN", 6: "QSA_E_HIP"}
 # qsa_dtype / qsa_kv_layout
-BF16, FP8_E4M3FN = 0, 1
+BF16, FP8_E4M3FN, FP16 = 0, 1, 2
 KV_PAGED, KV_COPACKED = 0, 1
 
 EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
@@ -113,6 +113,8 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype in (torch.float8_e4m3fn, torch.uint8):
         return FP8_E4M3FN
+    if t.dtype == torch.float16:
+        return FP16
     raise QsaError(E_DTYPE, f"unsupported tensor dtype {t.dtype}")
 
 

@@ -45,8 +45,8 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
     const bool empty = s->num_rows == 0 || s->width == 0;
     if (!empty && (!q || !kcache || !block_table || !ctx_lens || !row_to_req || !out))
         return fail(QSA_E_INVALID, "q, kcache, block_table, ctx_lens, row_to_req and out must be non-NULL");
-    if ((s->q_dtype != QSA_BF16 && s->q_dtype != QSA_FP8_E4M3FN) ||
-        (s->k_dtype != QSA_BF16 && s->k_dtype != QSA_FP8_E4M3FN))
+    auto known = [](int32_t d) { return d == QSA_BF16 || d == QSA_FP8_E4M3FN || d == QSA_FP16; };
+    if (!known(s->q_dtype) || !known(s->k_dtype))
         return fail(QSA_E_DTYPE, "unknown dtype (q %d, k %d)", s->q_dtype, s->k_dtype);
     if (s->q_dtype != s->k_dtype)
         return fail(QSA_E_DTYPE, "q and k dtypes differ (q %d, k %d)", s->q_dtype, s->k_dtype);
@@ -65,7 +65,7 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
     if (s->width > (1 << 24)) return fail(QSA_E_RANGE, "width = %d > 2^24", s->width);
     if ((int64_t)s->num_rows * s->out_stride > kMaxBytes / 4)
         return fail(QSA_E_RANGE, "num_rows * out_stride too large");
-    const int64_t elt = s->k_dtype == QSA_BF16 ? 2 : 1;
+    const int64_t elt = s->k_dtype == QSA_FP8_E4M3FN ? 1 : 2;
     const int64_t block_bytes = (int64_t)s->block_size * s->head_dim * elt +
                                 (s->kv_layout == QSA_KV_COPACKED ? 4 * (int64_t)s->block_size : 0);
     if (s->num_blocks > kMaxBytes / block_bytes) return fail(QSA_E_RANGE, "key pool too large");
@@ -127,7 +127,9 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     if (s->num_rows == 0 || s->width == 0) return ok();
     const bool fp8 = s->k_dtype == QSA_FP8_E4M3FN;
     const int64_t elt = fp8 ? 1 : 2;
-    qsa::LogitsPlan plan = qsa::plan_logits(fp8 ? 1 : 0, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
+    // the kernels' dtype codes are the qsa_dtype values
+    static_assert(QSA_BF16 == qsa::kBF16 && QSA_FP8_E4M3FN == qsa::kFP8 && QSA_FP16 == qsa::kFP16, "dtype codes");
+    qsa::LogitsPlan plan = qsa::plan_logits(s->k_dtype, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
                                                 s->out_stride);
     qsa::LogitsArgs a = {};
     a.q = q;
@@ -151,7 +153,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     a.num_chunks = (s->width + chunk_cols - 1) / chunk_cols;
     if ((int64_t)a.num_row_tiles * a.num_chunks > 0x7FFFFFFF)
         return fail(QSA_E_RANGE, "grid too large (%d row tiles x %d chunks)", a.num_row_tiles, a.num_chunks);
-    a.dtype = fp8 ? 1 : 0;
+    a.dtype = s->k_dtype;
     a.layout = s->kv_layout;
     a.num_blocks = s->num_blocks;
     a.out_stride = s->out_stride;

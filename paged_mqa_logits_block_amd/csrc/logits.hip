@@ -15,7 +15,7 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int
     // fp8, 32 or 64 heads, 4 rows per request on average (MTP verify), pool
     // blocks of a multiple of 64 columns: 4-row workgroups sharing each key
     // run; chunks sized for about four workgroups per CU
-    if (dtype == 1 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
+    if (dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
         block_size % kMtpRunCols == 0) {
         p.mtp = true;
         p.rows_per_tile = 4;
@@ -28,10 +28,11 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int
         p.tiles_per_prog = per * kMtpRunCols / 16;
         return p;
     }
-    // bf16, 4 heads, a single request holding all rows (a prefill chunk), pool
+    // bf16 or fp16, 4 heads, a single request holding all rows (a prefill chunk), pool
     // blocks of a multiple of 32 columns: the prefill variant, 64 rows per
     // workgroup, columns split so that about two workgroups run per CU
-    if (dtype == 0 && num_heads == 4 && num_reqs == 1 && num_rows >= 256 && block_size % 32 == 0 &&
+    if ((dtype == kBF16 || dtype == kFP16) && num_heads == 4 && num_reqs == 1 && num_rows >= 256 &&
+        block_size % 32 == 0 &&
         out_stride < ((int64_t)1 << 27)) {
         p.prefill = true;
         p.rows_per_tile = 16 * kPrefillWaves;
@@ -55,7 +56,7 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int
     // fp8 with 16+ heads: the looped variant, 4 key tiles per group and as many
     // groups per program as leave about four programs per SIMD; with 16 heads
     // and several rows per request (MTP verify rows) 4 rows share a program
-    if (dtype == 1 && num_heads >= 16) {
+    if (dtype == kFP8 && num_heads >= 16) {
         const int rows_per_req = num_reqs > 0 ? num_rows / num_reqs : 1;
         if (num_heads == 16 && rows_per_req >= 4) {
             p.rows_per_tile = 4;
@@ -75,9 +76,9 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int
 hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s, hipEvent_t e0,
                                hipEvent_t e1) {
     if (a.num_row_tiles == 0 || a.num_chunks == 0) return hipSuccess;
-    if (a.dtype == 0 && p.prefill) return launch_prefill(a, s, e0, e1);
-    if (a.dtype == 1 && p.mtp) return launch_mtp_fp8(a, s, e0, e1);
-    if (a.dtype == 1 && p.iters > 0) return launch_looped_fp8(a, p.rows_per_tile, s, e0, e1);
+    if (a.dtype != kFP8 && p.prefill) return launch_prefill(a, s, e0, e1);
+    if (a.dtype == kFP8 && p.mtp) return launch_mtp_fp8(a, s, e0, e1);
+    if (a.dtype == kFP8 && p.iters > 0) return launch_looped_fp8(a, p.rows_per_tile, s, e0, e1);
     return launch_decode(a, s, e0, e1);
 }
 

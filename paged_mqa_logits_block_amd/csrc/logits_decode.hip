@@ -27,9 +27,9 @@ namespace qsa {
 namespace {
 
 // H heads, MT stacked 16-row tiles, TPW 16-column tiles per program.
-template <bool FP8, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE>
+template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE>
 __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
-    typedef Frag<FP8> F;
+    typedef Frag<DT> F;
     constexpr int M = 16 * MT;
     static_assert(M % H == 0, "a row's heads must fit in the stacked tiles");
     constexpr int RT = M / H;  // rows per tile
@@ -340,33 +340,33 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     }
 }
 
-template <bool FP8, int H, int MT, int TPW>
+template <int DT, int H, int MT, int TPW>
 hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
-    const bool has_s = FP8 && (a.layout == 1 || a.kscale != nullptr);
+    const bool has_s = DT == kFP8 && (a.layout == 1 || a.kscale != nullptr);
     if (has_w && has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, true>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)
-        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, true, false>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, true>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true>), grid, block, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((paged_logits_kernel<FP8, H, MT, TPW, false, false>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
 }
 
 // (stacked tiles, tiles per program) by head count, as plan_logits chooses them
-template <bool FP8>
+template <int DT>
 hipError_t launch_heads(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     switch (a.num_heads) {
-        case 1: return launch_h<FP8, 1, 1, 4>(a, s, e0, e1);
-        case 2: return launch_h<FP8, 2, 1, 4>(a, s, e0, e1);
-        case 4: return launch_h<FP8, 4, 1, 4>(a, s, e0, e1);
-        case 8: return launch_h<FP8, 8, 1, 8>(a, s, e0, e1);
-        case 16: return launch_h<FP8, 16, 1, 8>(a, s, e0, e1);
-        case 32: return launch_h<FP8, 32, 2, 8>(a, s, e0, e1);
-        case 64: return launch_h<FP8, 64, 4, 8>(a, s, e0, e1);
+        case 1: return launch_h<DT, 1, 1, 4>(a, s, e0, e1);
+        case 2: return launch_h<DT, 2, 1, 4>(a, s, e0, e1);
+        case 4: return launch_h<DT, 4, 1, 4>(a, s, e0, e1);
+        case 8: return launch_h<DT, 8, 1, 8>(a, s, e0, e1);
+        case 16: return launch_h<DT, 16, 1, 8>(a, s, e0, e1);
+        case 32: return launch_h<DT, 32, 2, 8>(a, s, e0, e1);
+        case 64: return launch_h<DT, 64, 4, 8>(a, s, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -374,7 +374,12 @@ hipError_t launch_heads(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEv
 }  // namespace
 
 hipError_t launch_decode(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    return a.dtype == 0 ? launch_heads<false>(a, s, e0, e1) : launch_heads<true>(a, s, e0, e1);
+    switch (a.dtype) {
+        case kBF16: return launch_heads<kBF16>(a, s, e0, e1);
+        case kFP8: return launch_heads<kFP8>(a, s, e0, e1);
+        case kFP16: return launch_heads<kFP16>(a, s, e0, e1);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qsa

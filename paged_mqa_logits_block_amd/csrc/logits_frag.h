@@ -25,12 +25,12 @@ struct ColCursor {
     }
 };
 
-template <bool FP8>
+template <int DT>
 struct Frag;
 
 // bf16: v_mfma_f32_16x16x32_bf16, four K steps of 32 over D = 128.
 template <>
-struct Frag<false> {
+struct Frag<kBF16> {
     static constexpr int kSteps = 4;
     typedef bf16x8 T;
     // byte offset of lane l's slice inside a 16-element row of D (K step 0)
@@ -52,7 +52,7 @@ struct Frag<false> {
 // fp8 e4m3fn: v_mfma_scale_f32_16x16x128_f8f6f4 with unit (E8M0 127) scales,
 // one K step covers D = 128.
 template <>
-struct Frag<true> {
+struct Frag<kFP8> {
     static constexpr int kSteps = 1;
     typedef i32x8 T;
     __device__ static int lane_bytes(int l) { return (l >> 4) * 32; }
@@ -72,17 +72,38 @@ struct Frag<true> {
     static constexpr int kRowBytes = kD;
 };
 
+// fp16: v_mfma_f32_16x16x32_f16, four K steps of 32 over D = 128 (the same
+// operand layout as bf16).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <>
+struct Frag<kFP16> {
+    static constexpr int kSteps = 4;
+    typedef f16x8 T;
+    __device__ static int lane_bytes(int l) { return (l >> 4) * 16; }
+    __device__ static T load(const uint8_t *p, int s) { return *reinterpret_cast<const T *>(p + s * 64); }
+    __device__ static T zero() {
+        T z;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = (_Float16)0.0f;
+        return z;
+    }
+    __device__ static f32x4 mma(T a, T b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static constexpr int kRowBytes = kD * 2;
+};
+
 }  // namespace
 
 // One launcher per kernel file; each returns the launch status.
-// per-tile kernel (any dtype, 1..64 heads): logits_decode.hip
+// per-tile kernel (bf16, fp8 or fp16; 1..64 heads): logits_decode.hip
 hipError_t launch_decode(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // looped fp8 kernel (16+ heads, rows_per_tile from the plan): logits_looped.hip
 hipError_t launch_looped_fp8(const LogitsArgs &a, int rows_per_tile, hipStream_t s, hipEvent_t e0,
                              hipEvent_t e1);
 // 4-row fp8 kernel (32/64 heads): logits_mtp.hip
 hipError_t launch_mtp_fp8(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-// prefill kernel (bf16, 4 heads, one request): logits_prefill.hip
+// prefill kernel (bf16 or fp16, 4 heads, one request): logits_prefill.hip
 hipError_t launch_prefill(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 
 }  // namespace qsa

@@ -19,7 +19,7 @@ namespace {
 // table entry and one base address per group, the tiles at fixed offsets.
 template <int H, int MT, int TPI, bool HAS_W, bool HAS_SCALE, bool ONE_BLOCK>
 __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
-    typedef Frag<true> F;
+    typedef Frag<kFP8> F;
     constexpr int M = 16 * MT;
     constexpr int RT = M / H;
     static_assert(H >= 16 && RT >= 1 && RT <= 4, "looped variant: H >= 16, at most 4 rows");

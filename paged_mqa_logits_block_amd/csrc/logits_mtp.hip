@@ -23,7 +23,7 @@ constexpr int kMtpMaxRuns = kMtpMaxRunsPerGroup;  // runs per workgroup at most
 
 template <int H, bool HAS_W, bool HAS_SCALE>
 __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
-    typedef Frag<true> F;
+    typedef Frag<kFP8> F;
     constexpr int MT = H / 16;
     constexpr int D = kMtpDepth;
     static_assert(D % 2 == 0, "the LDS buffer parity follows the ring slot");

@@ -1,4 +1,4 @@
-// Paged MQA-logits scoring, prefill shape (bf16, 4 heads, one request, many rows).
+// Paged MQA-logits scoring, prefill shape (bf16 or fp16, 4 heads, one request, many rows).
 
 #include "logits_frag.h"
 
@@ -31,8 +31,23 @@ namespace {
 // stores, one descriptor per pair of output rows: a lane whose store must not
 // happen (outside the chunk, past the width) gets an offset beyond the
 // descriptor's range and the hardware drops it.
-typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// element type and 32x32x16 MFMA per input dtype (bf16 or fp16)
+template <int DT>
+struct PfType;
+template <>
+struct PfType<kBF16> {
+    typedef __bf16 E;
+    typedef __bf16 V __attribute__((ext_vector_type(8)));
+    __device__ static f32x16 mma(V a, V b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+};
+template <>
+struct PfType<kFP16> {
+    typedef _Float16 E;
+    typedef _Float16 V __attribute__((ext_vector_type(8)));
+    __device__ static f32x16 mma(V a, V b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
 typedef uint32_t pf_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPfKeyLds = 272;               // padded key in LDS (bytes)
@@ -41,7 +56,7 @@ constexpr int kPfDepth = 4;                  // runs in flight per workgroup
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data)
 constexpr int kDropOffset = (int)0x80000000u;  // beyond any descriptor range used here
 
-template <bool HAS_W, int NW>
+template <int DT, bool HAS_W, int NW>
 __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(LogitsArgs a) {
     constexpr int H = 4;
     constexpr int D = kPfDepth;
@@ -140,13 +155,15 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
         rok_l = a.row_to_req[row] == 0;
     }
     // resident Q: A operand of M tile mt, K step s: stacked pair 32 mt + l%32
-    pf_bf16x8 qa[2][8];
+    typedef PfType<DT> P;
+    typedef typename P::V pf_v8;
+    pf_v8 qa[2][8];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         const int m = 32 * mt + (l & 31);
-        const __bf16 *qr = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)(row0 + m / H) * H + m % H) * kD + 8 * gk;
+        const typename P::E *qr = reinterpret_cast<const typename P::E *>(a.q) + ((int64_t)(row0 + m / H) * H + m % H) * kD + 8 * gk;
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) qa[mt][s2] = *reinterpret_cast<const pf_bf16x8 *>(qr + 16 * s2);
+        for (int s2 = 0; s2 < 8; ++s2) qa[mt][s2] = *reinterpret_cast<const pf_v8 *>(qr + 16 * s2);
     }
     // Weights of the wave's rows, kept in LDS (registers are the limit here)
     // and read back per row in the epilogue: lane l stores row l / 4, head l % 4.
@@ -220,19 +237,19 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const uint8_t *kf = kbuf[k] + (l & 31) * kPfKeyLds + 16 * gk;
-                pf_bf16x8 b[8];
+                pf_v8 b[8];
 #pragma unroll
-                for (int s2 = 0; s2 < 8; ++s2) b[s2] = *reinterpret_cast<const pf_bf16x8 *>(kf + 32 * s2);
+                for (int s2 = 0; s2 < 8; ++s2) b[s2] = *reinterpret_cast<const pf_v8 *>(kf + 32 * s2);
                 const bool ok = __builtin_amdgcn_readfirstlane(okbuf[k]) != 0;
                 acc0 = f32x16{};
 #pragma unroll
                 for (int s2 = 0; s2 < 8; ++s2)
-                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s2], b[s2], acc0, 0, 0, 0);
+                    acc0 = P::mma(qa[0][s2], b[s2], acc0);
                 epilogue(1, st + k - 1, acc1, ok_prev);
                 acc1 = f32x16{};
 #pragma unroll
                 for (int s2 = 0; s2 < 8; ++s2)
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s2], b[s2], acc1, 0, 0, 0);
+                    acc1 = P::mma(qa[1][s2], b[s2], acc1);
                 epilogue(0, st + k, acc0, ok);
                 ok_prev = ok;
                 __syncthreads();
@@ -250,18 +267,21 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
     for (int st = nR; st < nsteps; ++st) store8(out_off(st, c0 + 32 * st + (l & 31)), ninf8);
 }
 
-template <bool HAS_W_, int NW>
+template <int DT, bool HAS_W_, int NW>
 static hipError_t launch_prefill_w(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64 * (NW + 1));
-    hipExtLaunchKernelGGL((prefill_logits_kernel<HAS_W_, NW>), grid, block, 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((prefill_logits_kernel<DT, HAS_W_, NW>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    return a.w ? launch_prefill_w<true, kPrefillWaves>(a, s, e0, e1)
-               : launch_prefill_w<false, kPrefillWaves>(a, s, e0, e1);
+    if (a.dtype == kFP16)
+        return a.w ? launch_prefill_w<kFP16, true, kPrefillWaves>(a, s, e0, e1)
+                   : launch_prefill_w<kFP16, false, kPrefillWaves>(a, s, e0, e1);
+    return a.w ? launch_prefill_w<kBF16, true, kPrefillWaves>(a, s, e0, e1)
+               : launch_prefill_w<kBF16, false, kPrefillWaves>(a, s, e0, e1);
 }
 
 }  // namespace qsa

@@ -7,6 +7,9 @@
 
 namespace qsa {
 
+// input dtype codes, equal to the qsa_dtype values: bf16, fp8 e4m3fn, fp16
+constexpr int kBF16 = 0, kFP8 = 1, kFP16 = 2;
+
 // Launch description of one qsa_paged_logits call, fully resolved on the host.
 struct LogitsArgs {
     const void *q;
@@ -26,7 +29,7 @@ struct LogitsArgs {
     int32_t cap;            // min(width, max_blocks * block_size)
     int32_t num_row_tiles;  // ceil(num_rows / rows per tile)
     int32_t num_chunks;     // column chunks per row tile
-    int32_t dtype;          // 0 bf16, 1 fp8 e4m3fn
+    int32_t dtype;          // kBF16, kFP8 or kFP16
     int32_t layout;         // 0 paged, 1 co-packed
     int32_t pad_;
     int64_t num_blocks;

@@ -41,9 +41,12 @@ import numpy as np
 HEAD_DIM = 128
 
 BF16_NAN = np.uint16(0x7FC0)
+FP16_NAN = np.uint16(0x7E00)
 FP8_NAN = np.uint8(0x7F)
 
 CONFIG_NAMES = ("tiny", "decode_verify", "single_row_mixed", "fp8_paged", "prefill_chunk")
+# the same shapes with fp16 q and keys (the pages' fp16 callers)
+FP16_CONFIG_NAMES = ("decode_verify_fp16", "prefill_chunk_fp16")
 
 
 @dataclasses.dataclass
@@ -51,7 +54,7 @@ class PagedInputs:
     """One batch of paged-logits inputs plus the top-k size."""
 
     name: str
-    dtype: str  # "bf16" or "fp8"
+    dtype: str  # "bf16", "fp16" or "fp8"
     layout: str  # "paged" or "copacked"
     num_heads: int
     head_dim: int
@@ -86,7 +89,7 @@ class PagedInputs:
         return np.clip(self.ctx_lens.astype(np.int64), 0, cap)
 
     def key_bytes_per_col(self) -> int:
-        if self.dtype == "bf16":
+        if self.dtype in ("bf16", "fp16"):
             return 2 * self.head_dim
         return self.head_dim + (4 if (self.layout == "copacked" or self.kscale is not None) else 0)
 
@@ -100,6 +103,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to the nearest IEEE binary16 (numpy's cast, ties to even);
+    returns the bits."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16).copy()
 
 
 def f32_to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
@@ -195,6 +204,8 @@ def build(
     qf[:, real_heads:, :] = 0.0
     if dtype == "bf16":
         q = f32_to_bf16_bits(qf)
+    elif dtype == "fp16":
+        q = f32_to_fp16_bits(qf)
     elif dtype == "fp8":
         q = f32_to_e4m3fn_codes(qf)
     else:
@@ -205,14 +216,15 @@ def build(
     # keys
     kf = rng.standard_normal((num_blocks, B, D), dtype=np.float32)
     kscale = None
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp16"):
         assert layout == "paged"
-        kc = f32_to_bf16_bits(kf)
+        kc = f32_to_bf16_bits(kf) if dtype == "bf16" else f32_to_fp16_bits(kf)
+        nan = BF16_NAN if dtype == "bf16" else FP16_NAN
         if poison:
-            kc[pool] = BF16_NAN
+            kc[pool] = nan
             for i, n in enumerate(kv):
                 if n % B and blocks_per_req[i]:
-                    kc[bt[i, blocks_per_req[i] - 1], n % B:, :] = BF16_NAN
+                    kc[bt[i, blocks_per_req[i] - 1], n % B:, :] = nan
     else:
         if fp8_scale:
             amax = np.max(np.abs(kf), axis=2)
@@ -252,7 +264,17 @@ def build(
 # ----------------------------------------------------------------------------
 
 def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> PagedInputs:
-    """The five named workloads, seeded 1..5 by default."""
+    """The five named workloads, seeded 1..5 by default, and fp16 variants of
+    decode_verify and prefill_chunk (same shapes and recipe, seeds 6 and 7)."""
+    if name in FP16_CONFIG_NAMES:
+        base = name[: -len("_fp16")]
+        return make_config_dtype(base, "fp16", seed=(6 if base == "decode_verify" else 7) if seed is None else seed,
+                                 poison=poison)
+    return make_config_dtype(name, "bf16", seed=seed, poison=poison)
+
+
+def make_config_dtype(name: str, dtype: str, seed: Optional[int] = None, poison: bool = False) -> PagedInputs:
+    """One named workload; ``dtype`` applies to the bf16 ones (bf16 or fp16)."""
     if name == "tiny":
         # 2 requests x 4 rows, contexts 1000 and 3000, block 16, pool of 256 blocks
         return build(name=name, seed=1 if seed is None else seed, req_rows=[4, 4],
@@ -263,7 +285,7 @@ def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> 
         ctx_req = rng.integers(16000, 32000, size=9, endpoint=True)
         return build(name=name, seed=int(rng.integers(1 << 31)), req_rows=[4] * 9,
                      ctx_rows=np.repeat(ctx_req, 4), num_heads=4, block_size=16,
-                     topk=2048, poison=poison)
+                     topk=2048, dtype=dtype, poison=poison)
     if name == "single_row_mixed":
         rng = np.random.default_rng(3 if seed is None else seed)
         ctx_req = np.floor(np.exp(rng.uniform(math.log(5000), math.log(65600), size=64)))
@@ -284,7 +306,7 @@ def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> 
         ctx = (pos + 1) // 4
         return build(name=name, seed=5 if seed is None else seed, req_rows=[16384],
                      ctx_rows=ctx, kv_lens=[28672], num_heads=4, block_size=64,
-                     max_blocks=448, width=28672, topk=2048, poison=poison)
+                     max_blocks=448, width=28672, topk=2048, dtype=dtype, poison=poison)
     raise KeyError(name)
 
 

@@ -12,9 +12,10 @@ def to_device(inp, device="cuda"):
     def t(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
-    if inp.dtype == "bf16":
-        q = t(inp.q.view(np.int16)).view(torch.bfloat16)
-        kc = t(inp.kcache.view(np.int16)).view(torch.bfloat16)
+    if inp.dtype in ("bf16", "fp16"):
+        td = torch.bfloat16 if inp.dtype == "bf16" else torch.float16
+        q = t(inp.q.view(np.int16)).view(td)
+        kc = t(inp.kcache.view(np.int16)).view(td)
     else:
         q = t(inp.q).view(torch.float8_e4m3fn)
         kc = t(inp.kcache) if inp.layout == "copacked" else t(inp.kcache).view(torch.float8_e4m3fn)

@@ -4,6 +4,10 @@ and compare it with the oracle under the gates the pages state.
 Gates:
 * bf16 logits: |g - o| <= 5e-5 + 5e-5 |o| elementwise (ROCm/ATOM PR #2651,
   Accuracy: rtol / atol 5e-5), and the -inf mask exact.
+* fp16 logits: the same gate.  The pages state none for fp16 (vLLM PR #62589,
+  Details, only says the dot runs in fp16 with fp32 accumulation); products of
+  two fp16 values are exact in float32 as bf16 ones are, so both differ from
+  the oracle only by the float32 accumulation order over the same sums.
 * fp8 logits: calc_diff(g, o) < 1e-3 over visible entries and the -inf mask
   exact (ROCm/aiter PR #4221, test gate).  The pages do not define calc_diff; it
   is read as 1 - 2 sum(g o) / sum(g^2 + o^2), the usual meaning of the name.  A
@@ -98,7 +102,7 @@ def assert_logits_match(g, o, inp, rows=None, label=""):
         assert np.all(np.isfinite(gr[:c])), f"{label} row {r}: non-finite visible logits"
         vis_g.append(gr[:c])
         vis_o.append(orow[:c])
-    if inp.dtype == "bf16":
+    if inp.dtype in ("bf16", "fp16"):
         for i, r in enumerate(rows):
             d = np.abs(vis_g[i].astype(np.float64) - vis_o[i])
             tol = bf16_tol(vis_o[i])
@@ -145,6 +149,6 @@ def assert_topk_banded(gi, oi, o_logits, tol_fn, label=""):
 
 
 def topk_tol(inp):
-    if inp.dtype == "bf16":
+    if inp.dtype in ("bf16", "fp16"):
         return lambda x: 2 * (5e-5 + 5e-5 * abs(x))
     return lambda x: 1e-3 * abs(x) + 1e-6

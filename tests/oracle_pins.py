@@ -44,6 +44,19 @@ def lib_e4m3fn(codes: np.ndarray) -> np.ndarray:
     return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
+def lib_fp16(bits: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def enc(dtype, values) -> np.ndarray:
+    """float32 values -> the input encoding of dtype (library / numpy casts)."""
+    if dtype == "bf16":
+        return bf16(values)
+    if dtype == "fp16":
+        return qsa_inputs.f32_to_fp16_bits(values)
+    return qsa_inputs.f32_to_e4m3fn_codes(np.asarray(values, dtype=np.float32))
+
+
 def bf16(values) -> np.ndarray:
     return qsa_inputs.f32_to_bf16_bits(np.asarray(values, dtype=np.float32))
 
@@ -70,9 +83,9 @@ def contiguous_keys_f64(inp, starts) -> list:
     for i in range(inp.num_reqs):
         n = int(inp.kv_lens[i])
         s0 = int(starts[i]) * B
-        if inp.dtype == "bf16":
+        if inp.dtype in ("bf16", "fp16"):
             flat = inp.kcache.reshape(-1, D)
-            out.append(lib_bf16(flat[s0:s0 + n]))
+            out.append((lib_bf16 if inp.dtype == "bf16" else lib_fp16)(flat[s0:s0 + n]))
         elif inp.layout == "paged":
             flat = inp.kcache.reshape(-1, D)
             sc = inp.kscale.reshape(-1).astype(np.float64) if inp.kscale is not None else None
@@ -134,6 +147,27 @@ def pin_bf16_matches_library(lib):
     assert np.array_equal(mine, lib_bf16(bits))
 
 
+def pin_fp16_matches_library(lib):
+    """Every one of the 65,536 binary16 codes against numpy's float16 -> float64."""
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    mine = np.array([lib.ora_fp16_to_double(int(c)) for c in codes])
+    ref = lib_fp16(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def pin_fp16_spec_points(lib):
+    # IEEE 754 binary16: bias 15, max 65504, min normal 2^-14, min subnormal 2^-24
+    f = lib.ora_fp16_to_double
+    assert f(0x3C00) == 1.0 and f(0xC000) == -2.0 and f(0x3555) == 1365 / 4096
+    assert f(0x7BFF) == 65504.0 and f(0x0400) == 2.0 ** -14
+    assert f(0x0001) == 2.0 ** -24 and f(0x03FF) == 1023 * 2.0 ** -24
+    assert f(0x7C00) == np.inf and f(0xFC00) == -np.inf and np.isnan(f(0x7E00))
+    assert f(0x0000) == 0.0 and np.signbit(f(0x8000))
+
+
 # ----------------------------------------------------------------------------
 # scoring
 # ----------------------------------------------------------------------------
@@ -142,7 +176,7 @@ def pin_one_hot_closed_form(lib):
     """q[r,h] = a_h * e_{j_h}: head h's dot is a_h * k[col, j_h]; the logit is
     sum_h w_h * max(a_h * k[col, j_h], 0).  Signs of a_h differ between heads,
     so a ReLU applied after the head sum (or none) changes the value."""
-    for dtype, layout in (("bf16", "paged"), ("fp8", "paged"), ("fp8", "copacked")):
+    for dtype, layout in (("bf16", "paged"), ("fp16", "paged"), ("fp8", "paged"), ("fp8", "copacked")):
         inp = small(seed=21, dtype=dtype, layout=layout, H=4, B=16, weights=True)
         starts = identity_table(inp)
         keys = contiguous_keys_f64(inp, starts)
@@ -155,7 +189,7 @@ def pin_one_hot_closed_form(lib):
         for r in range(R):
             for h in range(H):
                 qf[r, h, j[r, h]] = a[r, h]
-        inp.q = bf16(qf) if dtype == "bf16" else qsa_inputs.f32_to_e4m3fn_codes(qf)
+        inp.q = enc(dtype, qf)
         lg = oracle.paged_logits(inp, lib=lib)
         wv = inp.w.astype(np.float64)
         for r in range(R):
@@ -171,13 +205,14 @@ def pin_one_hot_closed_form(lib):
 def pin_gemv_nonnegative(lib):
     """With q >= 0 and k >= 0 every dot is >= 0, so the ReLU is the identity and
     sum_h w_h (q_h . k) = (sum_h w_h q_h) . k: a matrix-vector product."""
-    for dtype, layout, H in (("bf16", "paged", 1), ("bf16", "paged", 4), ("fp8", "copacked", 8)):
+    for dtype, layout, H in (("bf16", "paged", 1), ("bf16", "paged", 4), ("fp16", "paged", 4),
+                             ("fp8", "copacked", 8)):
         inp = small(seed=31, dtype=dtype, layout=layout, H=H, B=16, weights=(H > 1))
         starts = identity_table(inp)
-        if dtype == "bf16":
+        if dtype in ("bf16", "fp16"):
             inp.kcache = inp.kcache & np.uint16(0x7FFF)
             inp.q = inp.q & np.uint16(0x7FFF)
-            qd = lib_bf16(inp.q)
+            qd = (lib_bf16 if dtype == "bf16" else lib_fp16)(inp.q)
         else:
             B, D = inp.block_size, inp.head_dim
             inp.kcache[:, : B * D] &= np.uint8(0x7F)
@@ -209,7 +244,7 @@ def pin_relu_is_per_head(lib):
 
 def pin_zero_heads_add_zero(lib):
     """sglang PR #48649, Accuracy Tests: padded heads are zero, so they add 0."""
-    for dtype, layout in (("bf16", "paged"), ("fp8", "copacked")):
+    for dtype, layout in (("bf16", "paged"), ("fp16", "paged"), ("fp8", "copacked")):
         base = small(seed=51, dtype=dtype, layout=layout, H=4, weights=True)
         lg4 = oracle.paged_logits(base, lib=lib)
         pad = small(seed=51, dtype=dtype, layout=layout, H=4, weights=True)
@@ -255,7 +290,7 @@ def pin_mask_exact(lib):
 
 def pin_block_permutation_invariant(lib):
     """Moving blocks within the pool and rewriting the table is bitwise neutral."""
-    for dtype, layout in (("bf16", "paged"), ("fp8", "paged"), ("fp8", "copacked")):
+    for dtype, layout in (("bf16", "paged"), ("fp16", "paged"), ("fp8", "paged"), ("fp8", "copacked")):
         inp = small(seed=81, dtype=dtype, layout=layout, weights=True, pool=12)
         lg = oracle.paged_logits(inp, lib=lib)
         perm = np.random.default_rng(9).permutation(inp.num_blocks)

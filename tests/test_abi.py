@@ -30,6 +30,15 @@ def test_header_symbols_exported():
         assert ctypes.cast(getattr(m.lib, s), ctypes.c_void_p).value
 
 
+def test_fp16_validation():
+    """fp16 keys: paged layout only, no per-key scale, q and k dtypes equal."""
+    assert chk(shape(q_dtype=m.FP16, k_dtype=m.FP16, kv_layout=m.KV_COPACKED)) == m.E_UNSUPPORTED
+    assert chk(shape(q_dtype=m.FP16, k_dtype=m.FP16), ks=A) == m.E_INVALID
+    assert chk(shape(q_dtype=m.FP16, k_dtype=m.BF16)) == m.E_DTYPE
+    assert chk(shape(q_dtype=m.BF16, k_dtype=m.FP16)) == m.E_DTYPE
+    assert chk(shape(q_dtype=3, k_dtype=3)) == m.E_DTYPE
+
+
 def test_version():
     assert m.version().startswith("qsaidx ")
     assert "gfx950" in m.version()
@@ -54,6 +63,8 @@ def test_logits_valid_configurations():
     assert chk(shape(q_dtype=m.FP8_E4M3FN, k_dtype=m.FP8_E4M3FN), ks=A) == m.OK
     for H in (1, 2, 4, 8, 16, 32, 64):
         assert chk(shape(num_heads=H)) == m.OK
+    # fp16 q and keys, paged layout
+    assert chk(shape(q_dtype=m.FP16, k_dtype=m.FP16)) == m.OK
     for B in (16, 32, 48, 64, 400, 1024):
         assert chk(shape(block_size=B)) == m.OK
     # empty calls are valid whatever the pointers

@@ -48,9 +48,10 @@ def run_logits(inp, **kw):
 # ---------------------------------------------------------------------------
 
 SAMPLED_ROWS = {"prefill_chunk": [0, 1, 2, 3, 1000, 4095, 4096, 8191, 12000, 16380, 16381, 16382, 16383]}
+SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 
 
-@pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES)
+@pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES + qsa_inputs.FP16_CONFIG_NAMES)
 def test_config_logits_and_topk(name):
     inp = qsa_inputs.make_config(name, poison=True)
     rows = SAMPLED_ROWS.get(name)
@@ -87,7 +88,8 @@ EDGE_CTX = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1000]
 
 
 @pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 32, 64])
-@pytest.mark.parametrize("dtype,layout", [("bf16", "paged"), ("fp8", "paged"), ("fp8", "copacked")])
+@pytest.mark.parametrize("dtype,layout", [("bf16", "paged"), ("fp16", "paged"), ("fp8", "paged"),
+                                          ("fp8", "copacked")])
 def test_heads_and_dtypes(H, dtype, layout):
     ctx = [EDGE_CTX[(i * 5 + H) % len(EDGE_CTX)] for i in range(6)]
     inp = qsa_inputs.build(name="edge", seed=100 + H, req_rows=[2, 1, 3], ctx_rows=ctx,
@@ -171,6 +173,21 @@ def test_block_sizes_and_ragged_ctx(B):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"B{B}")
 
 
+@pytest.mark.parametrize("B", [48, 80, 400])
+@pytest.mark.parametrize("dtype,layout,H", [("bf16", "paged", 4), ("bf16", "paged", 16), ("fp16", "paged", 4),
+                                            ("fp8", "paged", 16), ("fp8", "copacked", 64)])
+def test_page_sizes_not_powers_of_two(B, dtype, layout, H):
+    """Block sizes that are multiples of 16 but not powers of two (page size
+    400 of the pages' callers): tiles and key groups straddle block edges at
+    other offsets, and 64-column key runs do not fit a block evenly."""
+    ctx = [1, B - 1, B, B + 1, 2 * B + 17, 5 * B, 3001, 4099]
+    inp = qsa_inputs.build(name="blkodd", seed=400 + B + H, req_rows=[3, 1, 4], ctx_rows=ctx,
+                           num_heads=H, block_size=B, dtype=dtype, layout=layout, weights=True, poison=True)
+    say("odd block", B, dtype, layout, H, "ctx", ctx)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"B{B} {dtype} {layout} H{H}")
+
+
 def _prefill_ctx(n, W, seed):
     """Causal visible counts of a chunk of n rows ending at column W, with
     edge counts mixed in (0, 1, a step boundary and its neighbours, past the
@@ -186,15 +203,16 @@ def _prefill_ctx(n, W, seed):
 
 @pytest.mark.parametrize("B", [32, 64, 128])
 @pytest.mark.parametrize("weights", [True, False])
-def test_prefill_many_rows_one_request(B, weights):
-    """bf16, 4 heads, one request holding a few hundred rows (the prefill
-    chunk shape, its own kernel): ragged row count and width, edge visible
-    counts, poisoned table slots and key tails."""
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_prefill_many_rows_one_request(B, weights, dtype):
+    """bf16 or fp16, 4 heads, one request holding a few hundred rows (the
+    prefill chunk shape, its own kernel): ragged row count and width, edge
+    visible counts, poisoned table slots and key tails."""
     n, W = 333, 1000
     ctx = _prefill_ctx(n, W, seed=B)
     inp = qsa_inputs.build(name="prefill", seed=900 + B, req_rows=[n], ctx_rows=ctx, kv_lens=[W],
-                           num_heads=4, block_size=B, width=W, weights=weights, poison=True)
-    say("prefill rows", n, "width", W, "block", B, "weights", weights)
+                           num_heads=4, block_size=B, width=W, weights=weights, dtype=dtype, poison=True)
+    say("prefill rows", n, "width", W, "block", B, "weights", weights, dtype)
     _, g = run_logits(inp)
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"prefill B{B}")
 
