@@ -111,11 +111,14 @@ typedef struct qsa_logits_shape {
  * fp8 scales are >= 0 (the scale is applied after the ReLU, which equals
  * applying it to the key only for non-negative scales).  Out-of-range indices are
  * never dereferenced: a row_to_req value outside [0, num_reqs) makes that row's
- * visible columns NaN, and a table entry outside [0, num_blocks) makes the 16
- * columns of every tile it would feed NaN.
+ * visible columns NaN, and a table entry outside [0, num_blocks) makes the
+ * columns it would feed NaN (with B a multiple of 16: the 16 columns of every
+ * 16-column tile it feeds).
  *
  * Compiled set (else QSA_E_UNSUPPORTED): D = 128; H in {1,2,4,8,16,32,64};
- * B a multiple of 16 in [16, 1024]; bf16 + PAGED, fp16 + PAGED, fp8 + PAGED,
+ * B in [1, 1024] (B = 1: one key per table entry, the per-token layout of
+ * ROCm/aiter PR #4221 before its KVBlockSize >= 1 commit; B not a multiple of 16
+ * takes a per-column gather); bf16 + PAGED, fp16 + PAGED, fp8 + PAGED,
  * fp8 + COPACKED.
  * Alignment (else QSA_E_ALIGN): q, kcache, out 16-byte aligned; out_stride % 4 == 0.
  * Range (else QSA_E_RANGE): W <= 1<<24; R*out_stride*4 and num_blocks*block

@@ -162,7 +162,9 @@ def paged_logits(q, kcache, block_table, ctx_lens, row_to_req, *, width: int, bl
     R = int(q.shape[0])
     _require(int(ctx_lens.numel()) == R and int(row_to_req.numel()) == R, "ctx_lens / row_to_req must have R entries")
     if out is None:
-        out = torch.empty((R, width), dtype=torch.float32, device=q.device)
+        # rows padded to a multiple of 4 floats (the ABI's out_stride rule);
+        # the result is the [R, width] view
+        out = torch.empty((R, (width + 3) & ~3), dtype=torch.float32, device=q.device)[:, :width]
     _require(out.dtype == torch.float32 and out.dim() == 2 and out.stride(1) == 1, "out must be f32 [R, >=width]")
     shape = make_shape(q, kcache, block_table, width=width, block_size=block_size, layout=layout,
                        out_stride=out.stride(0) if R > 0 else width)

@@ -60,8 +60,8 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
     const int H = s->num_heads;
     if (H > 64 || (H & (H - 1)) != 0)
         return fail(QSA_E_UNSUPPORTED, "num_heads = %d (built: 1, 2, 4, 8, 16, 32, 64)", H);
-    if (s->block_size % 16 != 0 || s->block_size > 1024)
-        return fail(QSA_E_UNSUPPORTED, "block_size = %d (built: multiples of 16 up to 1024)", s->block_size);
+    if (s->block_size > 1024)
+        return fail(QSA_E_UNSUPPORTED, "block_size = %d (built: 1 to 1024)", s->block_size);
     if (s->width > (1 << 24)) return fail(QSA_E_RANGE, "width = %d > 2^24", s->width);
     if ((int64_t)s->num_rows * s->out_stride > kMaxBytes / 4)
         return fail(QSA_E_RANGE, "num_rows * out_stride too large");

@@ -53,10 +53,11 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int
     // key bytes per column (long single-row and many-head fp8 shapes gained
     // 3..15%)
     p.tiles_per_prog = num_heads <= 4 ? 4 : 8;
-    // fp8 with 16+ heads: the looped variant, 4 key tiles per group and as many
+    // fp8 with 16+ heads and blocks of a multiple of 16 columns: the looped
+    // variant, 4 key tiles per group and as many
     // groups per program as leave about four programs per SIMD; with 16 heads
     // and several rows per request (MTP verify rows) 4 rows share a program
-    if (dtype == kFP8 && num_heads >= 16) {
+    if (dtype == kFP8 && num_heads >= 16 && block_size % 16 == 0) {
         const int rows_per_req = num_reqs > 0 ? num_rows / num_reqs : 1;
         if (num_heads == 16 && rows_per_req >= 4) {
             p.rows_per_tile = 4;

@@ -27,7 +27,11 @@ namespace qsa {
 namespace {
 
 // H heads, MT stacked 16-row tiles, TPW 16-column tiles per program.
-template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE>
+// GATHER: the block size is not a multiple of 16 (down to one key per block),
+// so a 16-column tile may straddle blocks: every lane reads the table entry of
+// its own column (which is also the accumulator column it holds) and gathers
+// its key slice from that block.
+template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE, bool GATHER>
 __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     typedef Frag<DT> F;
     constexpr int M = 16 * MT;
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     // Only for 4 or fewer heads: with more, most programs of the long mixed
     // single-row batch lie past their row's context and the guessed loads
     // are wasted there.
-    constexpr bool GUESS = H <= 4;
+    constexpr bool GUESS = H <= 4 && !GATHER;
     const int guess = GUESS ? min((int)(((int64_t)row0 * a.num_reqs) / a.num_rows), a.num_reqs - 1) : -1;
     int gblk[TPW];
     if constexpr (GUESS) {
@@ -184,7 +188,30 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         typename F::T b[TPW][F::kSteps];
         float kscale[TPW];
         bool ok[TPW];
-        if (any_live) {
+        if (any_live && GATHER) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int c = c0 + 16 * t + (l & 15);  // this lane's column
+                const int qb = c / a.block_size;
+                const int blk = req_ok ? bt[min(qb, a.max_blocks - 1)] : -1;
+                // the tile is live as a whole (columns past a row's count are
+                // masked at the store); a column whose entry is out of range
+                // reads block 0 and is scored NaN
+                ok[t] = c0 + 16 * t < vis && blk >= 0 && (int64_t)blk < a.num_blocks;
+                const int64_t bbase = ok[t] ? (int64_t)blk * a.block_bytes : 0;
+                const int slot = ok[t] ? c - qb * a.block_size : 0;
+                const uint8_t *kp = a.kcache + bbase + (int64_t)slot * a.key_stride + F::lane_bytes(l);
+#pragma unroll
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kp, s);
+                kscale[t] = 1.0f;
+                if (HAS_SCALE) {
+                    if (a.layout == 1)
+                        kscale[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[slot];
+                    else
+                        kscale[t] = a.kscale[(ok[t] ? (int64_t)blk * a.block_size : 0) + slot];
+                }
+            }
+        } else if (any_live) {
             int blk[TPW], slot0[TPW];
             ColCursor cur(c0, a.block_size);
             if (GUESS && req == guess) {
@@ -340,20 +367,26 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     }
 }
 
-template <int DT, int H, int MT, int TPW>
-hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int DT, int H, int MT, int TPW, bool GATHER>
+hipError_t launch_hg(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
     const bool has_s = DT == kFP8 && (a.layout == 1 || a.kscale != nullptr);
     if (has_w && has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true, GATHER>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false, GATHER>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true, GATHER>), grid, block, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false, GATHER>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
+}
+
+template <int DT, int H, int MT, int TPW>
+hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    return a.block_size % 16 == 0 ? launch_hg<DT, H, MT, TPW, false>(a, s, e0, e1)
+                                  : launch_hg<DT, H, MT, TPW, true>(a, s, e0, e1);
 }
 
 // (stacked tiles, tiles per program) by head count, as plan_logits chooses them

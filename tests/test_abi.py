@@ -65,7 +65,7 @@ def test_logits_valid_configurations():
         assert chk(shape(num_heads=H)) == m.OK
     # fp16 q and keys, paged layout
     assert chk(shape(q_dtype=m.FP16, k_dtype=m.FP16)) == m.OK
-    for B in (16, 32, 48, 64, 400, 1024):
+    for B in (1, 3, 8, 16, 32, 48, 64, 100, 200, 400, 1024):
         assert chk(shape(block_size=B)) == m.OK
     # empty calls are valid whatever the pointers
     assert chk(shape(num_rows=0), q=None, bt=None, ctx=None, r2r=None, out=None, kc=None) == m.OK
@@ -91,9 +91,8 @@ def test_logits_valid_configurations():
     (dict(head_dim=64), {}, m.E_UNSUPPORTED),
     (dict(num_heads=3), {}, m.E_UNSUPPORTED),
     (dict(num_heads=128), {}, m.E_UNSUPPORTED),
-    (dict(block_size=8), {}, m.E_UNSUPPORTED),
-    (dict(block_size=200), {}, m.E_UNSUPPORTED),
     (dict(block_size=2048), {}, m.E_UNSUPPORTED),
+    (dict(block_size=1025), {}, m.E_UNSUPPORTED),
     (dict(width=(1 << 24) + 16, out_stride=(1 << 24) + 16), {}, m.E_RANGE),
     (dict(num_blocks=1 << 51), {}, m.E_RANGE),
     ({}, dict(q=A + 4), m.E_ALIGN),

@@ -188,6 +188,40 @@ def test_page_sizes_not_powers_of_two(B, dtype, layout, H):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"B{B} {dtype} {layout} H{H}")
 
 
+@pytest.mark.parametrize("B", [1, 3, 7, 17, 100])
+@pytest.mark.parametrize("dtype,layout,H", [("bf16", "paged", 4), ("fp16", "paged", 2), ("bf16", "paged", 16),
+                                            ("fp8", "paged", 16), ("fp8", "copacked", 64)])
+def test_block_sizes_not_multiples_of_16(B, dtype, layout, H):
+    """Block sizes down to one key per table entry (the per-token layout): a
+    16-column tile straddles blocks, every lane gathers its own column.  The
+    tables are seeded permutations, so neighbouring columns sit in unrelated
+    blocks; contexts end inside and at the edges of blocks and tiles."""
+    ctx = [1, 2, B, B + 1, 15, 16, 17, 33 * B + 5, 1000, 1999]
+    inp = qsa_inputs.build(name="blkgather", seed=700 + B + H, req_rows=[4, 2, 4], ctx_rows=ctx,
+                           num_heads=H, block_size=B, dtype=dtype, layout=layout, weights=True, poison=True)
+    say("gather block", B, dtype, layout, H, "ctx", ctx)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"B{B} {dtype} {layout} H{H}")
+
+
+def test_block_size_one_invalid_entry_gives_nan_in_its_column_only():
+    """With one key per block a bad table entry spoils exactly its column."""
+    inp = qsa_inputs.build(name="blk1 bad", seed=771, req_rows=[4], ctx_rows=[300] * 4, kv_lens=[300],
+                           num_heads=4, block_size=1)
+    inp.block_table[0, 37] = inp.num_blocks + 5
+    say("block 1 invalid entry")
+    _, g = run_logits(inp)
+    x = g.cpu().numpy()
+    assert np.all(np.isnan(x[:, 37]))
+    keep = np.ones(inp.width, dtype=bool)
+    keep[37] = False
+    o = oracle.paged_logits(inp.__class__(**{**inp.__dict__, "block_table": np.where(
+        inp.block_table >= inp.num_blocks, 0, inp.block_table).astype(np.int32)}))
+    assert np.all(np.isfinite(x[:, :300][:, keep[:300]]))
+    d = np.abs(x[:, :300][:, keep[:300]].astype(np.float64) - o[:, :300][:, keep[:300]])
+    assert np.all(d <= 5e-5 + 5e-5 * np.abs(o[:, :300][:, keep[:300]]))
+
+
 def _prefill_ctx(n, W, seed):
     """Causal visible counts of a chunk of n rows ending at column W, with
     edge counts mixed in (0, 1, a step boundary and its neighbours, past the
@@ -279,8 +313,13 @@ def test_ctx_clamping_and_width():
     assert_logits_match(b[:, :50], oracle.paged_logits(inp), inp, label="clamp")
     m = pytest.importorskip("paged_mqa_logits_block_amd")
     with pytest.raises(m.QsaError) as e:
-        gpu_logits(inp, dev)  # unpadded stride 50
-    assert e.value.status == m.E_ALIGN
+        gpu_logits(inp, dev, out=torch.empty((inp.num_rows, 50), dtype=torch.float32, device="cuda"))
+    assert e.value.status == m.E_ALIGN  # unpadded stride 50
+    # without `out` the binding pads the rows itself and returns the [R, 50] view
+    g = gpu_logits(inp, dev)
+    torch.cuda.synchronize()
+    assert tuple(g.shape) == (inp.num_rows, 50) and g.stride(0) == 52
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label="clamp padded")
 
 
 def test_untouched_stride_tail_and_nan_canaries():
