@@ -56,6 +56,8 @@ DESCRIPTIONS = {
                           "ctx U[16000,32000], block 16, top-k 2048",
     "prefill_chunk_fp16": "prefill_chunk with fp16 q/k: 1 request, 16384 rows, 4 heads, D=128, "
                           "ctx (pos+1)//4, block 64, top-k 2048",
+    "fp8_paged_kvb1": "fp8_paged with one key per block (per-token co-packed layout, 132 B blocks): "
+                      "16 requests x 4 rows, 64 heads, fp8, kv_len 32768, top-k 2048",
 }
 
 
@@ -90,7 +92,7 @@ def scoring_kernel(inp):
     if (inp.dtype == "fp8" and inp.num_heads in (32, 64) and inp.num_rows == 4 * inp.num_reqs
             and inp.block_size % 64 == 0):
         return "mtp_fp8_kernel"
-    if inp.dtype == "fp8" and inp.num_heads >= 16:
+    if inp.dtype == "fp8" and inp.num_heads >= 16 and inp.block_size % 16 == 0:
         return "looped_logits_kernel"
     return "paged_logits_kernel"
 

@@ -47,6 +47,8 @@ FP8_NAN = np.uint8(0x7F)
 CONFIG_NAMES = ("tiny", "decode_verify", "single_row_mixed", "fp8_paged", "prefill_chunk")
 # the same shapes with fp16 q and keys (the pages' fp16 callers)
 FP16_CONFIG_NAMES = ("decode_verify_fp16", "prefill_chunk_fp16")
+# fp8_paged with one key per table entry (the per-token co-packed layout)
+KVB1_CONFIG_NAMES = ("fp8_paged_kvb1",)
 
 
 @dataclasses.dataclass
@@ -264,8 +266,16 @@ def build(
 # ----------------------------------------------------------------------------
 
 def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> PagedInputs:
-    """The five named workloads, seeded 1..5 by default, and fp16 variants of
-    decode_verify and prefill_chunk (same shapes and recipe, seeds 6 and 7)."""
+    """The five named workloads, seeded 1..5 by default; fp16 variants of
+    decode_verify and prefill_chunk (same shapes and recipe, seeds 6 and 7);
+    fp8_paged with one key per block (seed 8)."""
+    if name == "fp8_paged_kvb1":
+        kv_len, next_n, reqs = 32768, 4, 16
+        ctx = [kv_len - next_n + n + 1 for _ in range(reqs) for n in range(next_n)]
+        return build(name=name, seed=8 if seed is None else seed, req_rows=[next_n] * reqs,
+                     ctx_rows=ctx, kv_lens=[kv_len] * reqs, num_heads=64, block_size=1,
+                     dtype="fp8", layout="copacked", weights=True, max_blocks=kv_len,
+                     width=32768, topk=2048, poison=poison)
     if name in FP16_CONFIG_NAMES:
         base = name[: -len("_fp16")]
         return make_config_dtype(base, "fp16", seed=(6 if base == "decode_verify" else 7) if seed is None else seed,

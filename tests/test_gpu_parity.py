@@ -51,7 +51,8 @@ SAMPLED_ROWS = {"prefill_chunk": [0, 1, 2, 3, 1000, 4095, 4096, 8191, 12000, 163
 SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 
 
-@pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES + qsa_inputs.FP16_CONFIG_NAMES)
+@pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES + qsa_inputs.FP16_CONFIG_NAMES +
+                         qsa_inputs.KVB1_CONFIG_NAMES)
 def test_config_logits_and_topk(name):
     inp = qsa_inputs.make_config(name, poison=True)
     rows = SAMPLED_ROWS.get(name)
