@@ -83,14 +83,13 @@ def scoring_kernel(inp):
     """The scoring kernel the library picks for this shape (the same rule as
     its planner): the prefill variant for bf16 or fp16, 4 heads and one request with
     256+ rows and blocks of a multiple of 32 columns; the 4-row variant for fp8
-    with 32/64 heads, 4 rows per request and blocks of a multiple of 64
-    columns; the looped variant for other fp8 shapes with 16+ heads; the
-    per-tile variant otherwise."""
+    with 32/64 heads and 4 rows per request; the looped variant for other fp8
+    shapes with 16+ heads and blocks of a multiple of 16 columns; the per-tile
+    variant otherwise."""
     if (inp.dtype in ("bf16", "fp16") and inp.num_heads == 4 and inp.num_reqs == 1 and inp.num_rows >= 256
             and inp.block_size % 32 == 0):
         return "prefill_logits_kernel"
-    if (inp.dtype == "fp8" and inp.num_heads in (32, 64) and inp.num_rows == 4 * inp.num_reqs
-            and inp.block_size % 64 == 0):
+    if inp.dtype == "fp8" and inp.num_heads in (32, 64) and inp.num_rows == 4 * inp.num_reqs:
         return "mtp_fp8_kernel"
     if inp.dtype == "fp8" and inp.num_heads >= 16 and inp.block_size % 16 == 0:
         return "looped_logits_kernel"

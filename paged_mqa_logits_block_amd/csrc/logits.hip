@@ -15,8 +15,7 @@ LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int
     // fp8, 32 or 64 heads, 4 rows per request on average (MTP verify), pool
     // blocks of a multiple of 64 columns: 4-row workgroups sharing each key
     // run; chunks sized for about four workgroups per CU
-    if (dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
-        block_size % kMtpRunCols == 0) {
+    if (dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs) {
         p.mtp = true;
         p.rows_per_tile = 4;
         p.m_tiles = num_heads / 16;

@@ -21,16 +21,24 @@ constexpr int kMtpKeyLds = 144;               // padded key in LDS (bytes)
 constexpr int kMtpDepth = 4;                  // runs in flight
 constexpr int kMtpMaxRuns = kMtpMaxRunsPerGroup;  // runs per workgroup at most
 
-template <int H, bool HAS_W, bool HAS_SCALE>
+// GATHER: the pool block holds fewer than a run's 64 columns, or runs straddle
+// blocks (any block size not a multiple of 64, down to one key per block).
+// The table entry of every column of the chunk is staged in LDS once per
+// request (one round of loads before the ring starts), and each thread fetches
+// its key slice and, for every fourth thread, its key's scale from the block
+// of its own column; validity is kept per column.  Reading the entries from
+// LDS keeps them off the vector-memory counter that orders the key ring.
+template <int H, bool HAS_W, bool HAS_SCALE, bool GATHER>
 __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
     typedef Frag<kFP8> F;
     constexpr int MT = H / 16;
-    constexpr int D = kMtpDepth;
+    constexpr int D = GATHER ? 2 : kMtpDepth;  // ring depth (gather: fewer registers free for the per-thread addresses)
     static_assert(D % 2 == 0, "the LDS buffer parity follows the ring slot");
     __shared__ __align__(16) uint8_t kbuf[2][kMtpRun * kMtpKeyLds];
     __shared__ float sbuf[2][kMtpRun];
-    __shared__ int okbuf[2];
+    __shared__ int okbuf[2][GATHER ? kMtpRun : 1];  // per run, or per column (GATHER)
     __shared__ float obuf[4][kMtpRun * kMtpMaxRuns];
+    __shared__ int tcol[GATHER ? kMtpRun * kMtpMaxRuns : 1];  // GATHER: table entry per chunk column
 
     const int t = threadIdx.x;
     const int l = lane_id();
@@ -109,7 +117,32 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
             // runs the ring fetches past this workgroup's last one read block 0
             // (cached), not the next chunk's keys
             const int cend = min(vis, c0 + kMtpRun * nruns);
+            if constexpr (GATHER) {
+                const int32_t *btv = a.block_table + (req_ok ? (int64_t)req * a.max_blocks : 0);
+                for (int i = t; i < cend - c0; i += 256)
+                    tcol[i] = req_ok ? btv[min((c0 + i) / a.block_size, a.max_blocks - 1)] : -1;
+                __syncthreads();
+            }
+            // GATHER: thread t's column of the run and the block it lives in
+            auto fetch_gather = [&](i32x8 &kr, float &sr) -> bool {
+                const int col = cl + (t >> 2);
+                const int blk = col < cend ? tcol[col - c0] : -1;
+                const bool ok = (col < cend) & (blk >= 0) & ((int64_t)blk < a.num_blocks);
+                const int64_t bbase = ok ? (int64_t)blk * a.block_bytes : 0;
+                const int slot = ok ? col - (col / a.block_size) * a.block_size : 0;
+                kr = *reinterpret_cast<const i32x8 *>(a.kcache + bbase + (int64_t)slot * F::kRowBytes + 32 * (t & 3));
+                sr = 1.0f;
+                if (HAS_SCALE && (t & 3) == 0) {
+                    if (a.layout == 1)
+                        sr = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[slot];
+                    else
+                        sr = a.kscale[(ok ? (int64_t)blk * a.block_size : 0) + slot];
+                }
+                cl += kMtpRun;
+                return ok;
+            };
             auto fetch = [&](i32x8 &kr, float &sr) -> bool {
+                if constexpr (GATHER) return fetch_gather(kr, sr);
                 const int blk = req_ok ? bt[min(tq, a.max_blocks - 1)] : -1;
                 const bool ok = (cl < cend) & (blk >= 0) & ((int64_t)blk < a.num_blocks);
                 const int64_t bbase = ok ? (int64_t)blk * a.block_bytes : 0;
@@ -131,8 +164,15 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
             };
             auto put = [&](int buf, const i32x8 &kr, float sr, bool ok) {
                 *reinterpret_cast<i32x8 *>(kbuf[buf] + lane_key_lds) = kr;
-                if (t < kMtpRun) sbuf[buf][t] = sr;
-                if (t == 0) okbuf[buf] = ok;
+                if constexpr (GATHER) {
+                    if ((t & 3) == 0) {  // column t / 4 of the run
+                        sbuf[buf][t >> 2] = sr;
+                        okbuf[buf][t >> 2] = ok;
+                    }
+                } else {
+                    if (t < kMtpRun) sbuf[buf][t] = sr;
+                    if (t == 0) okbuf[buf][0] = ok;
+                }
             };
             // scores of run j (in LDS buffer buf) into obuf
             auto score = [&](int j, int buf) {
@@ -169,7 +209,7 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
                 const float r1 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
                 const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(r0), __float_as_uint(r1), false, false);
                 const float val = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-                const bool ok = __builtin_amdgcn_readfirstlane(okbuf[buf]) != 0;
+                const bool ok = GATHER ? okbuf[buf][l] != 0 : __builtin_amdgcn_readfirstlane(okbuf[buf][0]) != 0;
                 const float sc = HAS_SCALE ? sbuf[buf][l] : 1.0f;
                 obuf[w][kMtpRun * j + l] = ok ? val * sc : qnan;
             };
@@ -218,23 +258,28 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
     }
 }
 
-template <int H>
-static hipError_t launch_mtp(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int H, bool G>
+static hipError_t launch_mtp_g(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(256);
     const bool has_w = a.w != nullptr;
     const bool has_s = a.layout == 1 || a.kscale != nullptr;
     if (has_w && has_s)
-        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, true, true>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, true, true, G>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)
-        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, true, false>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, true, false, G>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_s)
-        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, false, true>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, false, true, G>), grid, block, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, false, false>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((mtp_fp8_kernel<H, false, false, G>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+template <int H>
+static hipError_t launch_mtp(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    return a.block_size % kMtpRun == 0 ? launch_mtp_g<H, false>(a, s, e0, e1) : launch_mtp_g<H, true>(a, s, e0, e1);
+}
 
 hipError_t launch_mtp_fp8(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     return a.num_heads == 64 ? launch_mtp<64>(a, s, e0, e1) : launch_mtp<32>(a, s, e0, e1);

@@ -141,6 +141,24 @@ def test_fp8_four_row_requests(H, layout, shuffle):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"mtp4 H{H}")
 
 
+@pytest.mark.parametrize("B", [1, 3, 100])
+@pytest.mark.parametrize("H,layout", [(64, "copacked"), (32, "paged")])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_fp8_four_row_requests_gather(B, H, layout, shuffle):
+    """The 4-row fp8 variant with blocks that do not hold whole 64-column runs
+    (down to one key per block): table entries staged per column, each key
+    fetched from its own block, validity per column."""
+    reqs = 5
+    ctx = [3000, 2999, 2998, 2997, 65, 64, 63, 0, 1000, 997, 998, 999, 129, 128, 127, 1,
+           1500, 1499, 1498, 1497]
+    inp = qsa_inputs.build(name="mtp4 gather", seed=860 + B + H + (3 if shuffle else 0), req_rows=[4] * reqs,
+                           ctx_rows=ctx, num_heads=H, block_size=B, dtype="fp8", layout=layout,
+                           weights=True, width=3004, poison=True, shuffle_rows=shuffle)
+    say("fp8 4-row gather", B, H, layout, "shuffle", shuffle)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"mtp4 gather B{B} H{H}")
+
+
 def test_fp8_four_row_requests_long():
     """The 4-row fp8 variant at a size where each workgroup walks several key
     runs (16 requests x 16,384 columns: 4 runs of 64 columns per workgroup,
