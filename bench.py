@@ -58,6 +58,8 @@ DESCRIPTIONS = {
                           "ctx (pos+1)//4, block 64, top-k 2048",
     "fp8_paged_kvb1": "fp8_paged with one key per block (per-token co-packed layout, 132 B blocks): "
                       "16 requests x 4 rows, 64 heads, fp8, kv_len 32768, top-k 2048",
+    "fp8_paged_shuffled": "fp8_paged with the keys of each co-packed KVB=64 block preshuffled in "
+                          "16x16-byte tiles: 16 requests x 4 rows, 64 heads, kv_len 32768, top-k 2048",
 }
 
 

@@ -72,7 +72,15 @@ typedef enum qsa_kv_layout {
      * each block is block_size*head_dim key bytes (key of slot s at byte
      * s*head_dim) followed by block_size little-endian f32 scales (slot s at
      * byte block_size*head_dim + 4*s); block stride block_size*(head_dim+4).  */
-    QSA_KV_COPACKED = 1
+    QSA_KV_COPACKED = 1,
+    /* fp8 only, co-packed with the keys preshuffled in 16x16-byte tiles
+     * (ROCm/aiter PR #4221, preshuffle commit and the commit that unifies both
+     * layouts as one coordinate space with two stride vectors): the scale tail
+     * is as in QSA_KV_COPACKED; in the key section, byte d of slot s sits at
+     * (s/16)*16*head_dim + (d/16)*256 + (s%16)*16 + d%16 (each group of 16
+     * slots is stored as head_dim/16 chunks of 16 slots x 16 bytes).
+     * block_size must be a multiple of 16.                                     */
+    QSA_KV_COPACKED_SHUFFLED = 2
 } qsa_kv_layout;
 
 typedef struct qsa_logits_shape {
@@ -98,7 +106,7 @@ typedef struct qsa_logits_shape {
  *   w           [R][H] f32, or NULL for w = 1.
  *   kcache      key pool in kv_layout (see qsa_kv_layout).
  *   kscale      QSA_KV_PAGED + fp8: [num_blocks][B] f32 or NULL (scale 1).
- *               Must be NULL for bf16, fp16 and QSA_KV_COPACKED.
+ *               Must be NULL for bf16, fp16 and the co-packed layouts.
  *   block_table [num_reqs][max_blocks] int32 pool block indices.
  *   ctx_lens    [R] int32 visible columns per row.
  *   row_to_req  [R] int32 row -> block_table row.
@@ -119,7 +127,7 @@ typedef struct qsa_logits_shape {
  * B in [1, 1024] (B = 1: one key per table entry, the per-token layout of
  * ROCm/aiter PR #4221 before its KVBlockSize >= 1 commit; B not a multiple of 16
  * takes a per-column gather); bf16 + PAGED, fp16 + PAGED, fp8 + PAGED,
- * fp8 + COPACKED.
+ * fp8 + COPACKED, fp8 + COPACKED_SHUFFLED (B a multiple of 16).
  * Alignment (else QSA_E_ALIGN): q, kcache, out 16-byte aligned; out_stride % 4 == 0.
  * Range (else QSA_E_RANGE): W <= 1<<24; R*out_stride*4 and num_blocks*block
  * bytes below 2^62.

@@ -82,6 +82,7 @@ class OracleError(RuntimeError):
 
 _GUARD = 64
 _DTYPE_CODES = {"bf16": 0, "fp8": 1, "fp16": 2}
+_LAYOUT_CODES = {"paged": 0, "copacked": 1, "copacked_shuffled": 2}
 _SENTINEL = 1.2345e300
 
 
@@ -122,7 +123,7 @@ def paged_logits(inp, rows: Optional[Sequence[int]] = None, threads: int = 0,
     out = buf[: n * inp.width].reshape(n, inp.width)
     st = lib.ora_paged_logits(
         _ptr(q), _DTYPE_CODES[inp.dtype], _ptr(w), _ptr(kc),
-        0 if inp.layout == "paged" else 1, _ptr(ks), _i32(bt), _i32(ctx), _i32(r2r),
+        _LAYOUT_CODES[inp.layout], _ptr(ks), _i32(bt), _i32(ctx), _i32(r2r),
         inp.num_rows, inp.num_heads, inp.head_dim, inp.block_size, inp.num_reqs,
         inp.max_blocks, inp.num_blocks, inp.width, _ptr(sel), n, _ptr(out), threads)
     if st != 0:

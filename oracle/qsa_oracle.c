@@ -124,14 +124,22 @@ static int fetch_key(double *kd, int dtype, int layout, const void *kcache, cons
         if (kscale)
             s = (double)kscale[(int64_t)blk * block_size + slot];
     } else {
-        /* co-packed block: block_size key rows of head_dim bytes, then
-         * block_size little-endian f32 scales */
+        /* co-packed block: block_size keys of head_dim bytes, then block_size
+         * little-endian f32 scales */
         const uint8_t *base = (const uint8_t *)kcache +
                               (int64_t)blk * block_size * (head_dim + 4);
         float sf;
-        k = base + (int64_t)slot * head_dim;
         memcpy(&sf, base + (int64_t)block_size * head_dim + 4 * slot, sizeof sf);
         s = (double)sf;
+        if (layout == 2) {
+            /* preshuffled keys (ROCm/aiter PR #4221, preshuffle commit): each
+             * group of 16 slots is head_dim/16 chunks of 16 slots x 16 bytes */
+            const uint8_t *g = base + (int64_t)(slot / 16) * 16 * head_dim;
+            for (int d = 0; d < head_dim; ++d)
+                kd[d] = ora_e4m3fn_to_double(g[(d / 16) * 256 + (slot % 16) * 16 + d % 16]) * s;
+            return ORA_OK;
+        }
+        k = base + (int64_t)slot * head_dim;
     }
     /* dequantise, then dot: k_f[d] = fp8(k[d]) * scale */
     for (int d = 0; d < head_dim; ++d)
@@ -161,6 +169,8 @@ int ora_paged_logits(const void *q, int dtype, const float *w, const void *kcach
     if (dtype != 0 && dtype != 1 && dtype != 2)
         return ORA_E_ARG;
     if (dtype != 1 && layout != 0)
+        return ORA_E_ARG;
+    if (layout < 0 || layout > 2 || (layout == 2 && (block_size % 16 != 0 || head_dim % 16 != 0)))
         return ORA_E_ARG;
     if (!rows)
         n_rows = num_rows;

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "QSA_OK", 1: "QSA_E_INVALID", 2: "QSA_E_DTYPE", 3: "QSA_E_UNS
                 4: "QSA_E_RANGE", 5: "QSA_E_ALIGN", 6: "QSA_E_HIP"}
 # qsa_dtype / qsa_kv_layout
 BF16, FP8_E4M3FN, FP16 = 0, 1, 2
-KV_PAGED, KV_COPACKED = 0, 1
+KV_PAGED, KV_COPACKED, KV_COPACKED_SHUFFLED = 0, 1, 2
 
 EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
             "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_last_error",

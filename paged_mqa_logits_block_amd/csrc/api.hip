@@ -50,10 +50,13 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
         return fail(QSA_E_DTYPE, "unknown dtype (q %d, k %d)", s->q_dtype, s->k_dtype);
     if (s->q_dtype != s->k_dtype)
         return fail(QSA_E_DTYPE, "q and k dtypes differ (q %d, k %d)", s->q_dtype, s->k_dtype);
-    if (s->kv_layout != QSA_KV_PAGED && s->kv_layout != QSA_KV_COPACKED)
+    if (s->kv_layout != QSA_KV_PAGED && s->kv_layout != QSA_KV_COPACKED && s->kv_layout != QSA_KV_COPACKED_SHUFFLED)
         return fail(QSA_E_INVALID, "unknown kv_layout %d", s->kv_layout);
-    if (s->kv_layout == QSA_KV_COPACKED && s->k_dtype != QSA_FP8_E4M3FN)
-        return fail(QSA_E_UNSUPPORTED, "the co-packed layout holds fp8 keys only");
+    const bool copacked = s->kv_layout != QSA_KV_PAGED;
+    if (copacked && s->k_dtype != QSA_FP8_E4M3FN)
+        return fail(QSA_E_UNSUPPORTED, "the co-packed layouts hold fp8 keys only");
+    if (s->kv_layout == QSA_KV_COPACKED_SHUFFLED && s->block_size % 16 != 0)
+        return fail(QSA_E_UNSUPPORTED, "the preshuffled layout needs block_size %% 16 == 0 (got %d)", s->block_size);
     if (kscale && (s->k_dtype != QSA_FP8_E4M3FN || s->kv_layout != QSA_KV_PAGED))
         return fail(QSA_E_INVALID, "kscale applies to fp8 keys in the paged layout only");
     if (s->head_dim != 128) return fail(QSA_E_UNSUPPORTED, "head_dim = %d (only 128 is built)", s->head_dim);
@@ -67,7 +70,7 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
         return fail(QSA_E_RANGE, "num_rows * out_stride too large");
     const int64_t elt = s->k_dtype == QSA_FP8_E4M3FN ? 1 : 2;
     const int64_t block_bytes = (int64_t)s->block_size * s->head_dim * elt +
-                                (s->kv_layout == QSA_KV_COPACKED ? 4 * (int64_t)s->block_size : 0);
+                                (copacked ? 4 * (int64_t)s->block_size : 0);
     if (s->num_blocks > kMaxBytes / block_bytes) return fail(QSA_E_RANGE, "key pool too large");
     if ((int64_t)s->num_reqs * s->max_blocks > ((int64_t)1 << 40))
         return fail(QSA_E_RANGE, "block table too large");
@@ -129,7 +132,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     const int64_t elt = fp8 ? 1 : 2;
     // the kernels' dtype codes are the qsa_dtype values
     static_assert(QSA_BF16 == qsa::kBF16 && QSA_FP8_E4M3FN == qsa::kFP8 && QSA_FP16 == qsa::kFP16, "dtype codes");
-    qsa::LogitsPlan plan = qsa::plan_logits(s->k_dtype, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
+    qsa::LogitsPlan plan = qsa::plan_logits(s->k_dtype, s->kv_layout, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
                                                 s->out_stride);
     qsa::LogitsArgs a = {};
     a.q = q;
@@ -158,7 +161,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     a.num_blocks = s->num_blocks;
     a.out_stride = s->out_stride;
     a.key_stride = s->head_dim * elt;
-    a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout == QSA_KV_COPACKED ? 4 * s->block_size : 0);
+    a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout != QSA_KV_PAGED ? 4 * s->block_size : 0);
     a.scale_offset = (int64_t)s->block_size * a.key_stride;
     a.iters = plan.iters;
     hipError_t e = qsa::launch_paged_logits(a, plan, static_cast<hipStream_t>(stream),

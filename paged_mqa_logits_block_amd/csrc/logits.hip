@@ -6,16 +6,18 @@
 namespace qsa {
 
 
-LogitsPlan plan_logits(int dtype, int num_heads, int num_rows, int num_reqs, int width, int block_size,
-                       int64_t out_stride) {
+LogitsPlan plan_logits(int dtype, int layout, int num_heads, int num_rows, int num_reqs, int width,
+                       int block_size, int64_t out_stride) {
     LogitsPlan p;
     p.iters = 0;
     p.prefill = false;
     p.mtp = false;
-    // fp8, 32 or 64 heads, 4 rows per request on average (MTP verify), pool
-    // blocks of a multiple of 64 columns: 4-row workgroups sharing each key
-    // run; chunks sized for about four workgroups per CU
-    if (dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs) {
+    // fp8, 32 or 64 heads, 4 rows per request on average (MTP verify): 4-row
+    // workgroups sharing each key run (any block size for block-flat keys,
+    // whole 64-column runs per block for preshuffled ones); chunks sized for
+    // about four workgroups per CU
+    if (dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
+        (layout != 2 || block_size % kMtpRunCols == 0)) {
         p.mtp = true;
         p.rows_per_tile = 4;
         p.m_tiles = num_heads / 16;

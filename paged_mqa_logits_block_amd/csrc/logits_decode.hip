@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                 for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kp, s);
                 kscale[t] = 1.0f;
                 if (HAS_SCALE) {
-                    if (a.layout == 1)
+                    if (a.layout != 0)
                         kscale[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[slot];
                     else
                         kscale[t] = a.kscale[(ok[t] ? (int64_t)blk * a.block_size : 0) + slot];
@@ -239,11 +239,16 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                 const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
                 const int tslot = ok[t] ? slot0[t] : 0;
                 const uint8_t *kt = a.kcache + bbase + (int64_t)tslot * a.key_stride;
+                if constexpr (DT == kFP8) {
+                    // one K step; slot0 is a multiple of 16: kt is a 16-token group
+                    b[t][0] = load_key_frag_fp8(kt, l, a.layout == 2);
+                } else {
 #pragma unroll
-                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kt + lane_key, s);
+                    for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kt + lane_key, s);
+                }
                 kscale[t] = 1.0f;
                 if (HAS_SCALE) {
-                    if (a.layout == 1)
+                    if (a.layout != 0)
                         kscale[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
                     else
                         kscale[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
@@ -371,7 +376,7 @@ template <int DT, int H, int MT, int TPW, bool GATHER>
 hipError_t launch_hg(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
-    const bool has_s = DT == kFP8 && (a.layout == 1 || a.kscale != nullptr);
+    const bool has_s = DT == kFP8 && (a.layout != 0 || a.kscale != nullptr);
     if (has_w && has_s)
         hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true, GATHER>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)

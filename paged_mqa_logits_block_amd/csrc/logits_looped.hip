@@ -93,7 +93,6 @@ __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
             // group ahead, scoring of the current group.  A tile past the
             // visible range or with an out-of-range table entry loads from
             // block 0 and is not scored.
-            const int lane_key = (l & 15) * (int)a.key_stride + F::lane_bytes(l);
             // the table stage and the key stage each walk the columns with a cursor
             ColCursor tab(c0, a.block_size), key(c0, a.block_size);
             auto fetch_table = [&](int (&blk)[TPI]) {
@@ -121,15 +120,15 @@ __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
                     key.r += 16 * TPI;
                     const bool wrap = key.r >= a.block_size;
                     key.r = wrap ? 0 : key.r;
-                    const uint8_t *kb = a.kcache + bbase + (int64_t)slot0 * F::kRowBytes + lane_key;
-                    const float *sb = HAS_SCALE ? (a.layout == 1 ? reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)
+                    const uint8_t *kg = a.kcache + bbase + (int64_t)slot0 * F::kRowBytes;  // first 16-token group
+                    const float *sb = HAS_SCALE ? (a.layout != 0 ? reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)
                                                                  : a.kscale + (bok ? (int64_t)blk[0] * a.block_size : 0))
                                                  + slot0 + (l & 15)
                                                 : nullptr;
 #pragma unroll
                     for (int t = 0; t < TPI; ++t) {
                         ok[t] = bok & (cg + 16 * t < vis);
-                        b[t] = F::load(kb + 16 * t * F::kRowBytes, 0);
+                        b[t] = load_key_frag_fp8(kg + 16 * t * F::kRowBytes, l, a.layout == 2);
                         sc[t] = HAS_SCALE ? sb[16 * t] : 1.0f;
                     }
                 } else {
@@ -140,10 +139,10 @@ __global__ __launch_bounds__(64) void looped_logits_kernel(LogitsArgs a) {
                         const int64_t bbase = ok[t] ? (int64_t)blk[t] * a.block_bytes : 0;
                         const int tslot = ok[t] ? key.r : 0;
                         key.step(a.block_size);
-                        b[t] = F::load(a.kcache + bbase + (int64_t)tslot * a.key_stride + lane_key, 0);
+                        b[t] = load_key_frag_fp8(a.kcache + bbase + (int64_t)tslot * a.key_stride, l, a.layout == 2);
                         sc[t] = 1.0f;
                         if (HAS_SCALE) {
-                            if (a.layout == 1)
+                            if (a.layout != 0)
                                 sc[t] = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[tslot + (l & 15)];
                             else
                                 sc[t] = a.kscale[(ok[t] ? (int64_t)blk[t] * a.block_size : 0) + tslot + (l & 15)];
@@ -240,7 +239,7 @@ static void launch_looped_b(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, h
 template <int H, int MT, int TPI>
 hipError_t launch_looped(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const bool has_w = a.w != nullptr;
-    const bool has_s = a.layout == 1 || a.kscale != nullptr;
+    const bool has_s = a.layout != 0 || a.kscale != nullptr;
     if (has_w && has_s)
         launch_looped_b<H, MT, TPI, true, true>(a, s, e0, e1);
     else if (has_w)

@@ -130,10 +130,12 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
                 const bool ok = (col < cend) & (blk >= 0) & ((int64_t)blk < a.num_blocks);
                 const int64_t bbase = ok ? (int64_t)blk * a.block_bytes : 0;
                 const int slot = ok ? col - (col / a.block_size) * a.block_size : 0;
+                // block-flat keys only: the planner sends preshuffled keys here
+                // only with blocks of whole 64-column runs (no gather)
                 kr = *reinterpret_cast<const i32x8 *>(a.kcache + bbase + (int64_t)slot * F::kRowBytes + 32 * (t & 3));
                 sr = 1.0f;
                 if (HAS_SCALE && (t & 3) == 0) {
-                    if (a.layout == 1)
+                    if (a.layout != 0)
                         sr = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[slot];
                     else
                         sr = a.kscale[(ok ? (int64_t)blk * a.block_size : 0) + slot];
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
                 kr = *reinterpret_cast<const i32x8 *>(a.kcache + bbase + (int64_t)slot * F::kRowBytes + 32 * t);
                 sr = 1.0f;
                 if (HAS_SCALE && t < kMtpRun) {
-                    if (a.layout == 1)
+                    if (a.layout != 0)
                         sr = reinterpret_cast<const float *>(a.kcache + bbase + a.scale_offset)[slot + t];
                     else
                         sr = a.kscale[(ok ? (int64_t)blk * a.block_size : 0) + slot + t];
@@ -163,7 +165,16 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
                 return ok;
             };
             auto put = [&](int buf, const i32x8 &kr, float sr, bool ok) {
-                *reinterpret_cast<i32x8 *>(kbuf[buf] + lane_key_lds) = kr;
+                if (!GATHER && a.layout == 2) {
+                    // a run's 8 KB are 4 preshuffled 16-token groups: thread t
+                    // holds 16 bytes (chunk k) of tokens i and i + 1 of group gq
+                    const int gq = t >> 6, k = (t & 63) >> 3, i = 2 * (t & 7);
+                    uint8_t *d = kbuf[buf] + (16 * gq + i) * kMtpKeyLds + 16 * k;
+                    *reinterpret_cast<i32x4 *>(d) = i32x4{kr[0], kr[1], kr[2], kr[3]};
+                    *reinterpret_cast<i32x4 *>(d + kMtpKeyLds) = i32x4{kr[4], kr[5], kr[6], kr[7]};
+                } else {
+                    *reinterpret_cast<i32x8 *>(kbuf[buf] + lane_key_lds) = kr;
+                }
                 if constexpr (GATHER) {
                     if ((t & 3) == 0) {  // column t / 4 of the run
                         sbuf[buf][t >> 2] = sr;
@@ -262,7 +273,7 @@ template <int H, bool G>
 static hipError_t launch_mtp_g(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(256);
     const bool has_w = a.w != nullptr;
-    const bool has_s = a.layout == 1 || a.kscale != nullptr;
+    const bool has_s = a.layout != 0 || a.kscale != nullptr;
     if (has_w && has_s)
         hipExtLaunchKernelGGL((mtp_fp8_kernel<H, true, true, G>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)

@@ -49,6 +49,8 @@ CONFIG_NAMES = ("tiny", "decode_verify", "single_row_mixed", "fp8_paged", "prefi
 FP16_CONFIG_NAMES = ("decode_verify_fp16", "prefill_chunk_fp16")
 # fp8_paged with one key per table entry (the per-token co-packed layout)
 KVB1_CONFIG_NAMES = ("fp8_paged_kvb1",)
+# fp8_paged with the keys of every co-packed block preshuffled in 16x16-byte tiles
+SHUFFLED_CONFIG_NAMES = ("fp8_paged_shuffled",)
 
 
 @dataclasses.dataclass
@@ -57,7 +59,7 @@ class PagedInputs:
 
     name: str
     dtype: str  # "bf16", "fp16" or "fp8"
-    layout: str  # "paged" or "copacked"
+    layout: str  # "paged", "copacked" or "copacked_shuffled"
     num_heads: int
     head_dim: int
     block_size: int
@@ -93,7 +95,7 @@ class PagedInputs:
     def key_bytes_per_col(self) -> int:
         if self.dtype in ("bf16", "fp16"):
             return 2 * self.head_dim
-        return self.head_dim + (4 if (self.layout == "copacked" or self.kscale is not None) else 0)
+        return self.head_dim + (4 if (self.layout != "paged" or self.kscale is not None) else 0)
 
 
 # ----------------------------------------------------------------------------
@@ -122,6 +124,16 @@ def f32_to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
 
     t = torch.from_numpy(np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0))
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def shuffle_keys_16x16(k8: np.ndarray) -> np.ndarray:
+    """Block-flat fp8 keys [blocks, B, D] -> the preshuffled key section
+    [blocks, B*D]: each group of 16 slots becomes D/16 chunks of 16 slots x 16
+    bytes (a layout transform of the input bytes only)."""
+    nb, B, D = k8.shape
+    assert B % 16 == 0 and D % 16 == 0
+    g = k8.reshape(nb, B // 16, 16, D // 16, 16)          # block, group, slot, chunk, byte
+    return np.ascontiguousarray(g.transpose(0, 1, 3, 2, 4)).reshape(nb, B * D)
 
 
 # ----------------------------------------------------------------------------
@@ -246,9 +258,12 @@ def build(
         if layout == "paged":
             kc = k8
             kscale = s
-        elif layout == "copacked":
+        elif layout in ("copacked", "copacked_shuffled"):
             kc = np.empty((num_blocks, B * (D + 4)), dtype=np.uint8)
-            kc[:, : B * D] = k8.reshape(num_blocks, B * D)
+            if layout == "copacked":
+                kc[:, : B * D] = k8.reshape(num_blocks, B * D)
+            else:
+                kc[:, : B * D] = shuffle_keys_16x16(k8)
             kc[:, B * D:] = s.astype("<f4").view(np.uint8).reshape(num_blocks, 4 * B)
         else:
             raise ValueError(layout)
@@ -268,13 +283,21 @@ def build(
 def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> PagedInputs:
     """The five named workloads, seeded 1..5 by default; fp16 variants of
     decode_verify and prefill_chunk (same shapes and recipe, seeds 6 and 7);
-    fp8_paged with one key per block (seed 8)."""
+    fp8_paged with one key per block (seed 8); fp8_paged with preshuffled keys
+    (seed 9)."""
     if name == "fp8_paged_kvb1":
         kv_len, next_n, reqs = 32768, 4, 16
         ctx = [kv_len - next_n + n + 1 for _ in range(reqs) for n in range(next_n)]
         return build(name=name, seed=8 if seed is None else seed, req_rows=[next_n] * reqs,
                      ctx_rows=ctx, kv_lens=[kv_len] * reqs, num_heads=64, block_size=1,
                      dtype="fp8", layout="copacked", weights=True, max_blocks=kv_len,
+                     width=32768, topk=2048, poison=poison)
+    if name == "fp8_paged_shuffled":
+        kv_len, next_n, reqs = 32768, 4, 16
+        ctx = [kv_len - next_n + n + 1 for _ in range(reqs) for n in range(next_n)]
+        return build(name=name, seed=9 if seed is None else seed, req_rows=[next_n] * reqs,
+                     ctx_rows=ctx, kv_lens=[kv_len] * reqs, num_heads=64, block_size=64,
+                     dtype="fp8", layout="copacked_shuffled", weights=True, max_blocks=512,
                      width=32768, topk=2048, poison=poison)
     if name in FP16_CONFIG_NAMES:
         base = name[: -len("_fp16")]

@@ -18,9 +18,9 @@ def to_device(inp, device="cuda"):
         kc = t(inp.kcache.view(np.int16)).view(td)
     else:
         q = t(inp.q).view(torch.float8_e4m3fn)
-        kc = t(inp.kcache) if inp.layout == "copacked" else t(inp.kcache).view(torch.float8_e4m3fn)
+        kc = t(inp.kcache) if inp.layout != "paged" else t(inp.kcache).view(torch.float8_e4m3fn)
     return types.SimpleNamespace(
         q=q, w=t(inp.w), kcache=kc, kscale=t(inp.kscale), block_table=t(inp.block_table),
         ctx_lens=t(inp.ctx_lens.astype(np.int32)), row_to_req=t(inp.row_to_req),
         width=inp.width, block_size=inp.block_size, topk=inp.topk,
-        layout=0 if inp.layout == "paged" else 1)
+        layout={"paged": 0, "copacked": 1, "copacked_shuffled": 2}[inp.layout])

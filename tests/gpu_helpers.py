@@ -67,7 +67,12 @@ def fp8_abs_bound(inp, rows, cols_per_row):
         wv = np.ones(H) if inp.w is None else np.abs(inp.w[r].astype(np.float64))
         blk = inp.block_table[req, cols // B]
         slot = cols % B
-        if inp.layout == "copacked":
+        if inp.layout == "copacked_shuffled":
+            d = np.arange(D)[None, :]
+            at = (slot[:, None] // 16) * 16 * D + (d // 16) * 256 + (slot[:, None] % 16) * 16 + d % 16
+            keys = inp.kcache[blk[:, None], at]
+            sc = inp.kcache[:, B * D:].copy().view("<f4").reshape(-1, B)[blk, slot].astype(np.float64)
+        elif inp.layout == "copacked":
             keys = inp.kcache[blk[:, None], slot[:, None] * D + np.arange(D)[None, :]]
             sc = inp.kcache[:, B * D:].copy().view("<f4").reshape(-1, B)[blk, slot].astype(np.float64)
         else:

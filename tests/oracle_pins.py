@@ -355,6 +355,25 @@ def pin_unit_scale_layouts_agree(lib):
     assert np.array_equal(lga, lgn) and np.array_equal(lga, lgb)
 
 
+def pin_preshuffled_layout_equals_block_flat(lib):
+    """ROCm/aiter PR #4221, preshuffle commit: only the intra-block key-byte
+    offset changes, so the same keys in the preshuffled co-packed layout must
+    give bitwise the same logits as in the block-flat one.  The generator's
+    shuffle is also checked against the stated offset of byte d of slot s."""
+    for H, B in ((4, 16), (64, 64), (16, 48)):
+        flat = small(seed=121, dtype="fp8", layout="copacked", H=H, B=B, weights=True)
+        shuf = small(seed=121, dtype="fp8", layout="copacked_shuffled", H=H, B=B, weights=True)
+        D = flat.head_dim
+        keys = flat.kcache[:, : B * D].reshape(-1, B, D)
+        sec = shuf.kcache[:, : B * D]
+        s_ = np.arange(B)[:, None]
+        d_ = np.arange(D)[None, :]
+        at = (s_ // 16) * 16 * D + (d_ // 16) * 256 + (s_ % 16) * 16 + d_ % 16
+        assert np.array_equal(sec[:, at], keys)
+        assert np.array_equal(shuf.kcache[:, B * D:], flat.kcache[:, B * D:])
+        assert np.array_equal(oracle.paged_logits(flat, lib=lib), oracle.paged_logits(shuf, lib=lib))
+
+
 def pin_weights_select_heads(lib):
     """w = e_h reduces the score to head h alone, i.e. the H = 1 problem on q[:, h]."""
     inp = small(seed=121, H=4, weights=True)

@@ -30,6 +30,19 @@ def test_header_symbols_exported():
         assert ctypes.cast(getattr(m.lib, s), ctypes.c_void_p).value
 
 
+def test_preshuffled_layout_validation():
+    """The preshuffled co-packed layout: fp8 only, blocks of a multiple of 16,
+    no separate scale array."""
+    f8 = dict(q_dtype=m.FP8_E4M3FN, k_dtype=m.FP8_E4M3FN, kv_layout=m.KV_COPACKED_SHUFFLED)
+    for B in (16, 48, 64, 400, 1024):
+        assert chk(shape(block_size=B, **f8)) == m.OK
+    for B in (1, 8, 100):
+        assert chk(shape(block_size=B, **f8)) == m.E_UNSUPPORTED
+    assert chk(shape(kv_layout=m.KV_COPACKED_SHUFFLED)) == m.E_UNSUPPORTED  # bf16
+    assert chk(shape(block_size=64, **f8), ks=A) == m.E_INVALID
+    assert chk(shape(kv_layout=3)) == m.E_INVALID
+
+
 def test_fp16_validation():
     """fp16 keys: paged layout only, no per-key scale, q and k dtypes equal."""
     assert chk(shape(q_dtype=m.FP16, k_dtype=m.FP16, kv_layout=m.KV_COPACKED)) == m.E_UNSUPPORTED

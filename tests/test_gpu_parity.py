@@ -52,7 +52,7 @@ SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 
 
 @pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES + qsa_inputs.FP16_CONFIG_NAMES +
-                         qsa_inputs.KVB1_CONFIG_NAMES)
+                         qsa_inputs.KVB1_CONFIG_NAMES + qsa_inputs.SHUFFLED_CONFIG_NAMES)
 def test_config_logits_and_topk(name):
     inp = qsa_inputs.make_config(name, poison=True)
     rows = SAMPLED_ROWS.get(name)
@@ -90,7 +90,7 @@ EDGE_CTX = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1000]
 
 @pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("dtype,layout", [("bf16", "paged"), ("fp16", "paged"), ("fp8", "paged"),
-                                          ("fp8", "copacked")])
+                                          ("fp8", "copacked"), ("fp8", "copacked_shuffled")])
 def test_heads_and_dtypes(H, dtype, layout):
     ctx = [EDGE_CTX[(i * 5 + H) % len(EDGE_CTX)] for i in range(6)]
     inp = qsa_inputs.build(name="edge", seed=100 + H, req_rows=[2, 1, 3], ctx_rows=ctx,
@@ -120,7 +120,7 @@ def test_fp8_many_heads_mtp_rows(H, layout, req_rows):
 
 
 @pytest.mark.parametrize("H", [32, 64])
-@pytest.mark.parametrize("layout", ["paged", "copacked"])
+@pytest.mark.parametrize("layout", ["paged", "copacked", "copacked_shuffled"])
 @pytest.mark.parametrize("shuffle", [False, True])
 def test_fp8_four_row_requests(H, layout, shuffle):
     """fp8, 32/64 heads, exactly 4 rows per request (the 4-row workgroup

@@ -38,6 +38,8 @@ MUTATIONS = {
     "fp8_subnormal": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
     "fp8_no_nan": ("if (e == 15 && m == 7)\n        return NAN;", ""),
     "bf16_shift": ("uint32_t u = ((uint32_t)bits) << 16;", "uint32_t u = ((uint32_t)bits) << 15;"),
+    "shuffle_transposed": ("g[(d / 16) * 256 + (slot % 16) * 16 + d % 16]", "g[(d / 16) * 16 + (slot % 16) * 256 + d % 16]"),
+    "shuffle_as_flat": ("g[(d / 16) * 256 + (slot % 16) * 16 + d % 16]", "g[(slot % 16) * head_dim + d]"),
     "fp16_bias": ("v = ldexp(1.0 + (double)m / 1024.0, e - 15);", "v = ldexp(1.0 + (double)m / 1024.0, e - 14);"),
     "fp16_subnormal": ("v = ldexp((double)m / 1024.0, -14);", "v = ldexp((double)m / 1024.0, -15);"),
     "fp16_as_bf16": ("return dtype == 0 ? ora_bf16_to_double(b) : ora_fp16_to_double(b);",
