@@ -60,6 +60,8 @@ DESCRIPTIONS = {
                       "16 requests x 4 rows, 64 heads, fp8, kv_len 32768, top-k 2048",
     "fp8_paged_shuffled": "fp8_paged with the keys of each co-packed KVB=64 block preshuffled in "
                           "16x16-byte tiles: 16 requests x 4 rows, 64 heads, kv_len 32768, top-k 2048",
+    "decode_verify_d64": "decode_verify with head dim 64: 9 requests x 4 MTP rows, 4 heads, D=64, bf16, "
+                         "ctx U[16000,32000], block 16, top-k 2048",
 }
 
 
@@ -88,6 +90,8 @@ def scoring_kernel(inp):
     with 32/64 heads and 4 rows per request; the looped variant for other fp8
     shapes with 16+ heads and blocks of a multiple of 16 columns; the per-tile
     variant otherwise."""
+    if inp.head_dim != 128:
+        return "paged_logits_kernel"
     if (inp.dtype in ("bf16", "fp16") and inp.num_heads == 4 and inp.num_reqs == 1 and inp.num_rows >= 256
             and inp.block_size % 32 == 0):
         return "prefill_logits_kernel"

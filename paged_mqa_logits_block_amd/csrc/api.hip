@@ -59,7 +59,8 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
         return fail(QSA_E_UNSUPPORTED, "the preshuffled layout needs block_size %% 16 == 0 (got %d)", s->block_size);
     if (kscale && (s->k_dtype != QSA_FP8_E4M3FN || s->kv_layout != QSA_KV_PAGED))
         return fail(QSA_E_INVALID, "kscale applies to fp8 keys in the paged layout only");
-    if (s->head_dim != 128) return fail(QSA_E_UNSUPPORTED, "head_dim = %d (only 128 is built)", s->head_dim);
+    if (s->head_dim != 128 && s->head_dim != 64)
+        return fail(QSA_E_UNSUPPORTED, "head_dim = %d (built: 64, 128)", s->head_dim);
     const int H = s->num_heads;
     if (H > 64 || (H & (H - 1)) != 0)
         return fail(QSA_E_UNSUPPORTED, "num_heads = %d (built: 1, 2, 4, 8, 16, 32, 64)", H);
@@ -132,7 +133,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     const int64_t elt = fp8 ? 1 : 2;
     // the kernels' dtype codes are the qsa_dtype values
     static_assert(QSA_BF16 == qsa::kBF16 && QSA_FP8_E4M3FN == qsa::kFP8 && QSA_FP16 == qsa::kFP16, "dtype codes");
-    qsa::LogitsPlan plan = qsa::plan_logits(s->k_dtype, s->kv_layout, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
+    qsa::LogitsPlan plan = qsa::plan_logits(s->k_dtype, s->kv_layout, s->head_dim, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
                                                 s->out_stride);
     qsa::LogitsArgs a = {};
     a.q = q;
@@ -161,6 +162,7 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     a.num_blocks = s->num_blocks;
     a.out_stride = s->out_stride;
     a.key_stride = s->head_dim * elt;
+    a.head_dim = s->head_dim;
     a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout != QSA_KV_PAGED ? 4 * s->block_size : 0);
     a.scale_offset = (int64_t)s->block_size * a.key_stride;
     a.iters = plan.iters;

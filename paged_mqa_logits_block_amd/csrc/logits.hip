@@ -6,17 +6,20 @@
 namespace qsa {
 
 
-LogitsPlan plan_logits(int dtype, int layout, int num_heads, int num_rows, int num_reqs, int width,
-                       int block_size, int64_t out_stride) {
+LogitsPlan plan_logits(int dtype, int layout, int head_dim, int num_heads, int num_rows, int num_reqs,
+                       int width, int block_size, int64_t out_stride) {
     LogitsPlan p;
     p.iters = 0;
     p.prefill = false;
     p.mtp = false;
+    // the looped, 4-row and prefill kernels are built for D = 128; other head
+    // dims take the per-tile kernel
+    const bool d128 = head_dim == 128;
     // fp8, 32 or 64 heads, 4 rows per request on average (MTP verify): 4-row
     // workgroups sharing each key run (any block size for block-flat keys,
     // whole 64-column runs per block for preshuffled ones); chunks sized for
     // about four workgroups per CU
-    if (dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
+    if (d128 && dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
         (layout != 2 || block_size % kMtpRunCols == 0)) {
         p.mtp = true;
         p.rows_per_tile = 4;
@@ -32,7 +35,7 @@ LogitsPlan plan_logits(int dtype, int layout, int num_heads, int num_rows, int n
     // bf16 or fp16, 4 heads, a single request holding all rows (a prefill chunk), pool
     // blocks of a multiple of 32 columns: the prefill variant, 64 rows per
     // workgroup, columns split so that about two workgroups run per CU
-    if ((dtype == kBF16 || dtype == kFP16) && num_heads == 4 && num_reqs == 1 && num_rows >= 256 &&
+    if (d128 && (dtype == kBF16 || dtype == kFP16) && num_heads == 4 && num_reqs == 1 && num_rows >= 256 &&
         block_size % 32 == 0 &&
         out_stride < ((int64_t)1 << 27)) {
         p.prefill = true;
@@ -58,7 +61,7 @@ LogitsPlan plan_logits(int dtype, int layout, int num_heads, int num_rows, int n
     // variant, 4 key tiles per group and as many
     // groups per program as leave about four programs per SIMD; with 16 heads
     // and several rows per request (MTP verify rows) 4 rows share a program
-    if (dtype == kFP8 && num_heads >= 16 && block_size % 16 == 0) {
+    if (d128 && dtype == kFP8 && num_heads >= 16 && block_size % 16 == 0) {
         const int rows_per_req = num_reqs > 0 ? num_rows / num_reqs : 1;
         if (num_heads == 16 && rows_per_req >= 4) {
             p.rows_per_tile = 4;

@@ -31,7 +31,9 @@ namespace {
 // so a 16-column tile may straddle blocks: every lane reads the table entry of
 // its own column (which is also the accumulator column it holds) and gathers
 // its key slice from that block.
-template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE, bool GATHER>
+// D: head dim, 128 or 64 (a template argument, so that D = 128 carries no
+// run-time test in the hot loop).
+template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE, bool GATHER, int D>
 __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     typedef Frag<DT> F;
     constexpr int M = 16 * MT;
@@ -61,6 +63,12 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
 
     const int l = lane_id();
     const int g = l >> 4;  // lane group
+    // head dim D = 128, or 64: the bf16/fp16 K steps past D/32, and the fp8
+    // lanes of lane groups past D/32, hold zeros (the fp8 MFMA's K is 128)
+    static_assert(D == 128 || D == 64, "head dim");
+    constexpr int dk = D >> 5;
+    constexpr int kRow = D * (DT == kFP8 ? 1 : 2);  // bytes of a q or key row
+    auto frag_on = [&](int s) { return DT == kFP8 ? (dk == 4 || g < dk) : s < dk; };
     const int tile = blockIdx.x / a.num_chunks;
     const int chunk = blockIdx.x - tile * a.num_chunks;
     const int row0 = tile * RT;
@@ -111,10 +119,10 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
         const int m = 16 * mt + (l & 15);
         const int row = row0 + m / H, h = m % H;
         const uint8_t *qrow = reinterpret_cast<const uint8_t *>(a.q) +
-                              ((int64_t)row * H + h) * F::kRowBytes + F::lane_bytes(l);
+                              ((int64_t)row * H + h) * kRow + F::lane_bytes(l);
 #pragma unroll
         for (int s = 0; s < F::kSteps; ++s)
-            qa[mt][s] = (row < a.num_rows) ? F::load(qrow, s) : F::zero();
+            qa[mt][s] = (row < a.num_rows && frag_on(s)) ? F::load(qrow, s) : F::zero();
     }
 
     // weights of the accumulator slots this lane holds: slot (mt, i) is stacked
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                 const int slot = ok[t] ? c - qb * a.block_size : 0;
                 const uint8_t *kp = a.kcache + bbase + (int64_t)slot * a.key_stride + F::lane_bytes(l);
 #pragma unroll
-                for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kp, s);
+                for (int s = 0; s < F::kSteps; ++s) b[t][s] = frag_on(s) ? F::load(kp, s) : F::zero();
                 kscale[t] = 1.0f;
                 if (HAS_SCALE) {
                     if (a.layout != 0)
@@ -241,10 +249,10 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                 const uint8_t *kt = a.kcache + bbase + (int64_t)tslot * a.key_stride;
                 if constexpr (DT == kFP8) {
                     // one K step; slot0 is a multiple of 16: kt is a 16-token group
-                    b[t][0] = load_key_frag_fp8(kt, l, a.layout == 2);
+                    b[t][0] = frag_on(0) ? load_key_frag_fp8(kt, l, a.layout == 2, kRow) : F::zero();
                 } else {
 #pragma unroll
-                    for (int s = 0; s < F::kSteps; ++s) b[t][s] = F::load(kt + lane_key, s);
+                    for (int s = 0; s < F::kSteps; ++s) b[t][s] = frag_on(s) ? F::load(kt + lane_key, s) : F::zero();
                 }
                 kscale[t] = 1.0f;
                 if (HAS_SCALE) {
@@ -276,7 +284,8 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int s = 0; s < F::kSteps; ++s) acc[mt] = F::mma(qa[mt][s], b[t][s], acc[mt]);
+                for (int s = 0; s < F::kSteps; ++s)
+                    if (DT == kFP8 || s < dk) acc[mt] = F::mma(qa[mt][s], b[t][s], acc[mt]);
 
             // head reduction: per stored row, sum of w * ReLU over its heads
             if (H <= 4) {
@@ -372,26 +381,29 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     }
 }
 
-template <int DT, int H, int MT, int TPW, bool GATHER>
+template <int DT, int H, int MT, int TPW, bool GATHER, int D>
 hipError_t launch_hg(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
     const bool has_s = DT == kFP8 && (a.layout != 0 || a.kscale != nullptr);
     if (has_w && has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true, GATHER>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false, GATHER>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true, GATHER>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false, GATHER>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
 }
 
 template <int DT, int H, int MT, int TPW>
 hipError_t launch_h(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    return a.block_size % 16 == 0 ? launch_hg<DT, H, MT, TPW, false>(a, s, e0, e1)
-                                  : launch_hg<DT, H, MT, TPW, true>(a, s, e0, e1);
+    if (a.head_dim == 64)
+        return a.block_size % 16 == 0 ? launch_hg<DT, H, MT, TPW, false, 64>(a, s, e0, e1)
+                                      : launch_hg<DT, H, MT, TPW, true, 64>(a, s, e0, e1);
+    return a.block_size % 16 == 0 ? launch_hg<DT, H, MT, TPW, false, 128>(a, s, e0, e1)
+                                  : launch_hg<DT, H, MT, TPW, true, 128>(a, s, e0, e1);
 }
 
 // (stacked tiles, tiles per program) by head count, as plan_logits chooses them

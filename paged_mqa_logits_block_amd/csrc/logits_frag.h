@@ -98,15 +98,17 @@ struct Frag<kFP16> {
 // (layouts 0 and 1) are 128 contiguous bytes per token; the preshuffled
 // co-packed layout (2) stores a 16-token group as 8 chunks of 16 tokens x 16
 // bytes (byte d of token i at (d / 16) * 256 + i * 16 + d % 16), so the 32
-// bytes are two 16-byte pieces 256 bytes apart.
-__device__ __forceinline__ i32x8 load_key_frag_fp8(const uint8_t *group, int l, bool shuffled) {
+// bytes are two 16-byte pieces 256 bytes apart (for any D: a group is 16 D
+// bytes, and a lane's pieces sit at the same offsets inside it).
+// row_bytes = D (128, or 64 with the caller zeroing lanes 32..63).
+__device__ __forceinline__ i32x8 load_key_frag_fp8(const uint8_t *group, int l, bool shuffled, int row_bytes = kD) {
     if (shuffled) {
         const uint8_t *p = group + (l & 15) * 16 + (l >> 4) * 512;
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(p);
         const i32x4 hi = *reinterpret_cast<const i32x4 *>(p + 256);
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    return *reinterpret_cast<const i32x8 *>(group + (l & 15) * kD + (l >> 4) * 32);
+    return *reinterpret_cast<const i32x8 *>(group + (l & 15) * row_bytes + (l >> 4) * 32);
 }
 
 }  // namespace

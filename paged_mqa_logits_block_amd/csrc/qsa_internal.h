@@ -31,7 +31,7 @@ struct LogitsArgs {
     int32_t num_chunks;     // column chunks per row tile
     int32_t dtype;          // kBF16, kFP8 or kFP16
     int32_t layout;         // 0 paged, 1 co-packed, 2 co-packed preshuffled
-    int32_t pad_;
+    int32_t head_dim;       // D: 128, or 64 (per-tile kernel only)
     int64_t num_blocks;
     int64_t out_stride;
     int64_t block_bytes;    // stride between pool blocks
@@ -62,8 +62,8 @@ constexpr int kMtpMaxRunsPerGroup = 16;
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillGroupsPerCU = 12 / (kPrefillWaves + 1);
 
-LogitsPlan plan_logits(int dtype, int layout, int num_heads, int num_rows, int num_reqs, int width,
-                       int block_size, int64_t out_stride);
+LogitsPlan plan_logits(int dtype, int layout, int head_dim, int num_heads, int num_rows, int num_reqs,
+                       int width, int block_size, int64_t out_stride);
 // start / stop (may be null) are recorded by the dispatch packet itself at the
 // kernel's start and end.
 hipError_t launch_paged_logits(const LogitsArgs &a, const LogitsPlan &p, hipStream_t s,

@@ -51,6 +51,8 @@ FP16_CONFIG_NAMES = ("decode_verify_fp16", "prefill_chunk_fp16")
 KVB1_CONFIG_NAMES = ("fp8_paged_kvb1",)
 # fp8_paged with the keys of every co-packed block preshuffled in 16x16-byte tiles
 SHUFFLED_CONFIG_NAMES = ("fp8_paged_shuffled",)
+# decode_verify with head dim 64
+D64_CONFIG_NAMES = ("decode_verify_d64",)
 
 
 @dataclasses.dataclass
@@ -284,7 +286,7 @@ def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> 
     """The five named workloads, seeded 1..5 by default; fp16 variants of
     decode_verify and prefill_chunk (same shapes and recipe, seeds 6 and 7);
     fp8_paged with one key per block (seed 8); fp8_paged with preshuffled keys
-    (seed 9)."""
+    (seed 9); decode_verify with head dim 64 (seed 10)."""
     if name == "fp8_paged_kvb1":
         kv_len, next_n, reqs = 32768, 4, 16
         ctx = [kv_len - next_n + n + 1 for _ in range(reqs) for n in range(next_n)]
@@ -299,6 +301,12 @@ def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> 
                      ctx_rows=ctx, kv_lens=[kv_len] * reqs, num_heads=64, block_size=64,
                      dtype="fp8", layout="copacked_shuffled", weights=True, max_blocks=512,
                      width=32768, topk=2048, poison=poison)
+    if name == "decode_verify_d64":
+        rng = np.random.default_rng(10 if seed is None else seed)
+        ctx_req = rng.integers(16000, 32000, size=9, endpoint=True)
+        return build(name=name, seed=int(rng.integers(1 << 31)), req_rows=[4] * 9,
+                     ctx_rows=np.repeat(ctx_req, 4), num_heads=4, head_dim=64, block_size=16,
+                     topk=2048, poison=poison)
     if name in FP16_CONFIG_NAMES:
         base = name[: -len("_fp16")]
         return make_config_dtype(base, "fp16", seed=(6 if base == "decode_verify" else 7) if seed is None else seed,

@@ -13,7 +13,11 @@ Gates:
   is read as 1 - 2 sum(g o) / sum(g^2 + o^2), the usual meaning of the name.  A
   global similarity can hide a few wrong columns, so every element is also held
   to the worst-case bound of float32 accumulation: with A = sum_h |w_h| s
-  sum_d |q_hd k8_d| (all magnitudes), |g - o| <= (D + H + 2) 2^-23 A.
+  sum_d |q_hd k8_d| (all magnitudes), |g - o| <= (K + H + 2) 2^-23 A, where
+  K = max(D, 128) is the length of the reduction: the fp8 MFMA reduces its
+  full K = 128 products per instruction, zero-padded lanes included when
+  D = 64 (measured: 91.8 units of 2^-23 A at D = 64, beyond the 63 any
+  sequential 64-term float32 sum allows).
 * top-k on identical float32 logits: exact set equality (the tie rule makes the
   answer unique).
 * top-k end to end: the sets may differ only among columns whose oracle score
@@ -56,7 +60,7 @@ def bf16_tol(o):
 
 
 def fp8_abs_bound(inp, rows, cols_per_row):
-    """(D + H + 2) 2^-23 * sum_h |w| s sum_d |q k8| for the given (row, cols)."""
+    """(max(D, 128) + H + 2) 2^-23 * sum_h |w| s sum_d |q k8| for the given (row, cols)."""
     D, H, B = inp.head_dim, inp.num_heads, inp.block_size
     qa = np.abs(oracle.decode_e4m3fn(np.arange(256, dtype=np.uint8)))
     qa = np.nan_to_num(qa)
@@ -81,7 +85,7 @@ def fp8_abs_bound(inp, rows, cols_per_row):
                   else inp.kscale[blk, slot].astype(np.float64))
         km = qa[keys]  # [n, D]
         A = (km @ qm.T) @ wv * np.abs(sc)
-        out.append((D + H + 2) * 2.0 ** -23 * A)
+        out.append((max(D, 128) + H + 2) * 2.0 ** -23 * A)
     return out
 
 

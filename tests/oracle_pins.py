@@ -205,9 +205,9 @@ def pin_one_hot_closed_form(lib):
 def pin_gemv_nonnegative(lib):
     """With q >= 0 and k >= 0 every dot is >= 0, so the ReLU is the identity and
     sum_h w_h (q_h . k) = (sum_h w_h q_h) . k: a matrix-vector product."""
-    for dtype, layout, H in (("bf16", "paged", 1), ("bf16", "paged", 4), ("fp16", "paged", 4),
-                             ("fp8", "copacked", 8)):
-        inp = small(seed=31, dtype=dtype, layout=layout, H=H, B=16, weights=(H > 1))
+    for dtype, layout, H, D in (("bf16", "paged", 1, 128), ("bf16", "paged", 4, 128), ("fp16", "paged", 4, 128),
+                                ("fp8", "copacked", 8, 128), ("bf16", "paged", 4, 64), ("fp8", "copacked", 4, 64)):
+        inp = small(seed=31, dtype=dtype, layout=layout, H=H, B=16, weights=(H > 1), head_dim=D)
         starts = identity_table(inp)
         if dtype in ("bf16", "fp16"):
             inp.kcache = inp.kcache & np.uint16(0x7FFF)

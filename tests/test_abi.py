@@ -76,6 +76,9 @@ def test_logits_valid_configurations():
     assert chk(shape(q_dtype=m.FP8_E4M3FN, k_dtype=m.FP8_E4M3FN), ks=A) == m.OK
     for H in (1, 2, 4, 8, 16, 32, 64):
         assert chk(shape(num_heads=H)) == m.OK
+    # head dim 64 (per-tile kernel), every dtype
+    assert chk(shape(head_dim=64)) == m.OK
+    assert chk(shape(head_dim=64, q_dtype=m.FP8_E4M3FN, k_dtype=m.FP8_E4M3FN, kv_layout=m.KV_COPACKED_SHUFFLED)) == m.OK
     # fp16 q and keys, paged layout
     assert chk(shape(q_dtype=m.FP16, k_dtype=m.FP16)) == m.OK
     for B in (1, 3, 8, 16, 32, 48, 64, 100, 200, 400, 1024):
@@ -101,7 +104,8 @@ def test_logits_valid_configurations():
     (dict(kv_layout=9), {}, m.E_INVALID),
     (dict(kv_layout=m.KV_COPACKED), {}, m.E_UNSUPPORTED),  # co-packed bf16
     ({}, dict(ks=A), m.E_INVALID),  # a scale with bf16 keys
-    (dict(head_dim=64), {}, m.E_UNSUPPORTED),
+    (dict(head_dim=96), {}, m.E_UNSUPPORTED),
+    (dict(head_dim=256), {}, m.E_UNSUPPORTED),
     (dict(num_heads=3), {}, m.E_UNSUPPORTED),
     (dict(num_heads=128), {}, m.E_UNSUPPORTED),
     (dict(block_size=2048), {}, m.E_UNSUPPORTED),

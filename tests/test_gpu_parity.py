@@ -52,7 +52,8 @@ SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 
 
 @pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES + qsa_inputs.FP16_CONFIG_NAMES +
-                         qsa_inputs.KVB1_CONFIG_NAMES + qsa_inputs.SHUFFLED_CONFIG_NAMES)
+                         qsa_inputs.KVB1_CONFIG_NAMES + qsa_inputs.SHUFFLED_CONFIG_NAMES +
+                         qsa_inputs.D64_CONFIG_NAMES)
 def test_config_logits_and_topk(name):
     inp = qsa_inputs.make_config(name, poison=True)
     rows = SAMPLED_ROWS.get(name)
@@ -239,6 +240,25 @@ def test_block_size_one_invalid_entry_gives_nan_in_its_column_only():
     assert np.all(np.isfinite(x[:, :300][:, keep[:300]]))
     d = np.abs(x[:, :300][:, keep[:300]].astype(np.float64) - o[:, :300][:, keep[:300]])
     assert np.all(d <= 5e-5 + 5e-5 * np.abs(o[:, :300][:, keep[:300]]))
+
+
+@pytest.mark.parametrize("dtype,layout", [("bf16", "paged"), ("fp16", "paged"), ("fp8", "paged"),
+                                          ("fp8", "copacked"), ("fp8", "copacked_shuffled")])
+@pytest.mark.parametrize("H,B,req_rows", [(4, 16, [4, 4, 4]), (16, 64, [4, 4, 4]), (64, 16, [4, 4, 4]),
+                                          (2, 3, [3, 1, 5]), (64, 48, [1, 2, 2])])
+def test_head_dim_64(dtype, layout, H, B, req_rows):
+    """Head dim 64 (the per-tile kernel for every shape): zero K steps for
+    bf16/fp16, zero lane groups in the fp8 MFMA; 4-row requests and many heads
+    that take other kernels at D = 128; block sizes with the per-column gather."""
+    if layout == "copacked_shuffled" and B % 16:
+        pytest.skip("the preshuffled layout needs blocks of a multiple of 16")
+    R = sum(req_rows)
+    ctx = [[1, 15, 16, 17, 64, 65, 1000, 1999, 2000, 7, 33, 500][i % 12] for i in range(R)]
+    inp = qsa_inputs.build(name="d64", seed=300 + H + B, req_rows=req_rows, ctx_rows=ctx, num_heads=H,
+                           head_dim=64, block_size=B, dtype=dtype, layout=layout, weights=True, poison=True)
+    say("head dim 64", dtype, layout, "H", H, "B", B)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"D64 {dtype} {layout} H{H} B{B}")
 
 
 def _prefill_ctx(n, W, seed):
