@@ -123,7 +123,7 @@ typedef struct qsa_logits_shape {
  * columns it would feed NaN (with B a multiple of 16: the 16 columns of every
  * 16-column tile it feeds).
  *
- * Compiled set (else QSA_E_UNSUPPORTED): D = 128; H in {1,2,4,8,16,32,64};
+ * Compiled set (else QSA_E_UNSUPPORTED): D in {64, 128}; H in {1,2,4,8,16,32,64};
  * B in [1, 1024] (B = 1: one key per table entry, the per-token layout of
  * ROCm/aiter PR #4221 before its KVBlockSize >= 1 commit; B not a multiple of 16
  * takes a per-column gather); bf16 + PAGED, fp16 + PAGED, fp8 + PAGED,
