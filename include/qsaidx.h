@@ -191,7 +191,7 @@ QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const in
 
 /* Bytes of workspace qsa_topk uses for this shape; 0 when every row is selected
  * by one workgroup whatever the workspace.  Host-only, no HIP call; k does not
- * change the size in this build. */
+ * change the size in this version of the library. */
 QSA_API int64_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t width, int32_t k);
 
 /* qsa_topk with its kernels timed by dispatch-recorded events (as
