@@ -102,12 +102,21 @@ def scoring_kernel(inp):
     return "paged_logits_kernel"
 
 
+def _code_only(text):
+    """Source text without comments, trailing blanks and blank lines: edits to
+    comments do not change what the counters measured."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_hash(kernel):
-    """Hash of the sources a scoring kernel is built from."""
+    """Hash of the code (comments stripped) a scoring kernel is built from."""
     h = hashlib.sha256()
     for f in (KERNEL_FILES[kernel], *COMMON_SOURCES):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

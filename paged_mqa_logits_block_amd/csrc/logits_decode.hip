@@ -12,11 +12,15 @@
 // Layout of the work:
 //  * one program = one wave64 = (row tile, column chunk); a row tile is RT rows
 //    whose RT*H (row, head) pairs fill MT stacked 16-row MFMA tiles;
-//  * a column chunk is TPW tiles of 16 key columns; B % 16 == 0 so a tile never
-//    straddles a pool block and costs one table lookup (a scalar load);
+//  * a column chunk is TPW tiles of 16 key columns; with B % 16 == 0 a tile
+//    never straddles a pool block and costs one table lookup (a scalar load);
+//    other block sizes take the per-column gather (GATHER below);
 //  * the key tile is loaded straight from the pool into the MFMA B operand:
-//    lane l reads key column (l % 16), 16 contiguous bytes per K step, so each
-//    load instruction moves 16 rows x 64 contiguous bytes;
+//    lane l reads key column (l % 16), 16 contiguous bytes per K step (bf16,
+//    fp16), so each load instruction moves 16 rows x 64 contiguous bytes, or
+//    32 bytes in one K step (fp8: contiguous, or two 16-byte pieces of a
+//    preshuffled 16-key group);
+//  * inputs: bf16, fp16 or fp8 q and keys (DT), head dim 128 or 64 (D);
 //  * Q (the A operand) stays in registers for the whole program;
 //  * accumulator lane l holds M rows 4*(l/16)..+3 of column l % 16; with
 //    m = row*H + head, the head sum is in-lane for H <= 4, plus one or two

@@ -47,3 +47,9 @@ def test_write_traffic_scales_and_averages(tmp_path, monkeypatch):
     assert bench.measured_traffic("decode_verify", k) == t["bytes_per_launch"]
     # another kernel's sources do not validate this entry
     assert bench.source_hash("prefill_logits_kernel") != t["source_hash"]
+
+
+def test_source_hash_ignores_comments_only():
+    code = "int a; // note\n/* block\n comment */\nint b;   \n\n"
+    assert bench._code_only(code) == bench._code_only("int a;\nint b;") == "int a;\nint b;"
+    assert bench._code_only("int a = 1;") != bench._code_only("int a = 2;")
