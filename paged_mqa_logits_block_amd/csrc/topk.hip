@@ -719,8 +719,15 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
         }
     }
     __syncthreads();
-    for (int p = t; p < k; p += kThreads) out[p] = (int32_t)kept[p];
+    // the k columns stay in sh.cand_key; the caller writes them to `out`
+    // (flush_kept) when their stores cannot hold up a wait on its prefetch
+    (void)out;
     return true;
+}
+
+// Writes the k column indices select_fast left in sh.cand_key.
+__device__ __forceinline__ void flush_kept(const Shared &sh, int k, int32_t *out) {
+    for (int p = threadIdx.x; p < k; p += kThreads) out[p] = (int32_t)sh.cand_key[p];
 }
 
 // Rows of a many-row call, round robin over a grid of workgroups that each take
@@ -731,7 +738,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
 // These loads are issued from inline assembly: the compiler then neither
 // knows of them nor orders the selection's own LDS accesses behind them (it
 // would, for the builtin form, wait for every one before any LDS access); the
-// wait for them is explicit.  Rows the register path does not take (longer than
+// wait for them is explicit.  A row's output indices are stored at the top of
+// the next iteration, before that iteration's prefetch is issued: stores and
+// loads retire in order on one counter, so stores issued after a prefetch would
+// make the next wait on the prefetch also wait out the stores' latency.  Rows the register path does not take (longer than
 // kStage, or refused by select_fast) are marked and selected after the loop by
 // the staged or streaming selection.
 constexpr int kRowsPerGroup = 2048;
@@ -784,6 +794,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
     int n = visible(row);
     if (fast_row(n)) prefetch(row, n);
     f32x4 x[kStageGroups];
+    int32_t *pend = nullptr;  // the previous row's output, its columns still in LDS
 #pragma unroll 1
     for (int m = 0;; ++m) {
         const int nxt = row + stride;
@@ -798,12 +809,18 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
 #pragma unroll
             for (int j = 0; j < kStageGroups; ++j) x[j] = pref[tt + kThreads * j];
         }
-        __syncthreads();  // pref has been read (and the previous row is done with LDS)
+        if (pend) {
+            flush_kept(sh, k, pend);
+            pend = nullptr;
+        }
+        __syncthreads();  // pref and the kept columns have been read (the previous row is done with LDS)
         if (more && fast_row(nn)) prefetch(nxt, nn);
         int32_t *out = a.idx_out + (int64_t)row * k;
         if (n <= k) {
             for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
-        } else if (!fast || !select_fast(sh, x, n, k, out)) {
+        } else if (fast && select_fast(sh, x, n, k, out)) {
+            pend = out;
+        } else {
             if (t == 0) later[m >> 5] |= 1u << (m & 31);
             any_later = true;
         }
@@ -812,6 +829,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         row = nxt;
         n = nn;
     }
+    if (pend) flush_kept(sh, k, pend);
     if (!any_later) return;
     __syncthreads();
 #pragma unroll 1
