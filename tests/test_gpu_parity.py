@@ -636,3 +636,51 @@ def test_prepared_and_timed_calls_match():
     pt()
     torch.cuda.synchronize()
     assert torch.equal(out, ref) and torch.equal(idx, ref_idx)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_verify", "fp8_paged"])
+def test_graph_capture_replay(name):
+    """Both calls captured into one HIP graph (scoring, then top-k with its
+    workspace): every replay equals the eager result bit for bit, with eager
+    calls on other inputs, into other outputs, between the replays."""
+    m = qsa()
+    inp = qsa_inputs.make_config(name)
+    other = qsa_inputs.make_config(name, seed=77)
+    dev, dev2 = to_device(inp), to_device(other)
+    say("graph replay", name)
+    s = torch.cuda.Stream()
+    out = torch.empty((inp.num_rows, inp.width), dtype=torch.float32, device="cuda")
+    idx = torch.empty((inp.num_rows, inp.topk), dtype=torch.int32, device="cuda")
+    out2 = torch.empty((other.num_rows, other.width), dtype=torch.float32, device="cuda")
+    idx2 = torch.empty((other.num_rows, other.topk), dtype=torch.int32, device="cuda")
+
+    def calls(d, o, i):
+        return (m.PreparedLogits(d.q, d.kcache, d.block_table, d.ctx_lens, d.row_to_req, o, width=d.width,
+                                 block_size=d.block_size, w=d.w, kscale=d.kscale, layout=d.layout, stream=s),
+                m.PreparedTopk(o, d.ctx_lens, d.topk, i, stream=s))
+
+    lg, tk = calls(dev, out, idx)
+    lg2, tk2 = calls(dev2, out2, idx2)
+    torch.cuda.synchronize()
+    lg()
+    tk()
+    torch.cuda.synchronize()
+    ref, ref_idx = out.clone(), idx.clone()
+    o_idx = oracle.topk(ref.cpu().numpy(), inp.ctx_lens, inp.topk)
+    assert_topk_exact(idx.cpu().numpy(), o_idx, label=f"{name} eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lg()
+        tk()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"{name} replay {r}: logits differ"
+        assert torch.equal(idx, ref_idx), f"{name} replay {r}: indices differ"
+        lg2()  # eager work on other inputs between the replays
+        tk2()
+        torch.cuda.synchronize()
