@@ -67,6 +67,7 @@ struct Shared {
     int ncand;
     int tie_col;
     uint32_t thr_key;
+    int ties_cut;  // some keys equal to the k-th are dropped (the column order decides)
     // split selection (resolve kernel)
     int split_above;   // columns of the row above the window
     int split_before;  // columns kept before this slice, known before the resolve
@@ -551,21 +552,26 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
 // ---- register-resident selection of a finite row ---------------------------
 //
 // The same selection as select_staged for the common case -- every visible
-// value finite, at most kCand values in the crossing bucket, and no tie at the
-// k-th value that the column order has to break among more than 64 members --
+// value finite, at most kCand values in the crossing bucket, and every value
+// equal to the k-th one kept (no tie that the column order has to break) --
 // with the row kept in registers and compared as floats, so that each pass
 // costs a few vector operations per element:
 //  * range: NaN-propagating max3/min3 (a NaN or an infinity sends the row to
 //    select_staged);
-//  * buckets: floor(vmax*s - v*s) with one fma, clamped to [0, kBins-3], i.e.
-//    monotone non-increasing in v, the same expression in every pass;
-//  * the kept set: v > T or (v == T and column <= Ct), T as a float (for
-//    finite values the float order with +0 == -0 is the key order).
+//  * buckets: 1 + floor(vmax*s - v*s) with one fma, clamped to [1, kBins-2],
+//    i.e. monotone non-increasing in v.  The fma's result f can fall below 0
+//    (vmax*s is rounded, and once vmax/span exceeds about 16K that rounding
+//    exceeds 1), hence the lower clamp.  Bucket b holds exactly the f in [b-1, b), the first bucket
+//    everything below 1 and the last everything from kBins-3 up, so the
+//    crossing bucket's members are found by two compares on f;
+//  * the kept set: v >= T as floats (for finite values the float order with
+//    +0 == -0 is the key order), which needs every key equal to T kept.
+// A row where the column order has to drop some keys equal to T is set aside.
 // The kept columns are ranked in column order into LDS and written with
 // contiguous stores.  Returns false, having written nothing, in any other case.
 
 __device__ __forceinline__ int fast_bucket(float v, float s, float off) {
-    return 1 + min((int)__builtin_fmaf(v, -s, off), kBins - 3);
+    return 1 + max(min((int)__builtin_fmaf(v, -s, off), kBins - 3), 0);
 }
 
 __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups], int n, int k, int32_t *out) {
@@ -581,11 +587,14 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     // is visible: the range is unchanged, and every count below tests the
     // column
     const int tail = n - 4 * (n4 - 1);  // visible columns of the last group, 1..4
+    // first thread of this wave, as a scalar: whether a wave's group j reaches
+    // past n is uniform, so waves whose columns are all visible skip the fixes
+    const int wt0 = __builtin_amdgcn_readfirstlane(t & ~63);
     float mx = x[0][0], mn = x[0][0];
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) {
         const int i = t + kThreads * j;
-        if (i >= n4 - 1) {
+        if (4 * (wt0 + 63 + kThreads * j) + 4 > n && i >= n4 - 1) {
 #pragma unroll
             for (int e = 1; e < 4; ++e) x[j][e] = e < tail ? x[j][e] : x[j][0];
         }
@@ -627,6 +636,9 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     // ---- the members of the crossing bucket, as (key, column) ------------
     if (t == 0) sh.ncand = 0;
     __syncthreads();
+    // fast_bucket(v) == bstar exactly when the fma's f lies in [f_lo, f_hi)
+    const float f_lo = bstar <= 1 ? -__builtin_inff() : (float)(bstar - 1);
+    const float f_hi = bstar >= kBins - 2 ? __builtin_inff() : (float)bstar;
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) {
         const int i = t + kThreads * j;
@@ -634,7 +646,8 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
         bool any = false;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            hit[e] = (4 * i + e < n) & (fast_bucket(x[j][e], sc, off) == bstar);
+            const float f = __builtin_fmaf(x[j][e], -sc, off);
+            hit[e] = (4 * i + e < n) & (f >= f_lo) & (f < f_hi);
             any |= hit[e];
         }
         if (ballot(any)) {
@@ -660,7 +673,6 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
 
     // ---- the k-th pair (T, Ct) -------------------------------------------
     uint32_t T;
-    int tie_col;
     if (nc <= 64) {
         if (w == 0) {
             const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
@@ -671,14 +683,21 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
                 const int cj = readlane(mc, j);
                 rank += (kj > mk || (kj == mk && cj < mc)) ? 1 : 0;
             }
-            if (l < nc && rank == need - 1) {
-                sh.thr_key = mk;
-                sh.tie_col = mc;
-            }
+            const bool is_kth = l < nc && rank == need - 1;
+            if (is_kth) sh.thr_key = mk;
+            // a key equal to the k-th at a later column would be dropped
+            const int kl = __builtin_ctzll(ballot(is_kth));
+            const uint32_t tk = (uint32_t)readlane((int)mk, kl);
+            const int tc = readlane(mc, kl);
+            const bool cut = ballot(l < nc && mk == tk && mc > tc) != 0ull;
+            if (l == 0) sh.ties_cut = cut;
         }
         __syncthreads();
         T = sh.thr_key;
-        tie_col = sh.tie_col;
+        if (sh.ties_cut) {
+            __syncthreads();
+            return false;
+        }
     } else {
         radix_select(sh, [&](auto f) {
             for (int j = t; j < nc; j += kThreads) f(sh.cand_key[j]);
@@ -687,22 +706,15 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             __syncthreads();
             return false;
         }
-        tie_col = 0x7FFFFFFF;
     }
     const float Tf = key_value(T);
 
     // ---- the kept set in column order, through LDS -----------------------
     uint32_t sel = 0u;
 #pragma unroll
-    for (int j = 0; j < kStageGroups; ++j) {
-        const int c0 = 4 * (t + kThreads * j);
+    for (int j = 0; j < kStageGroups; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v = x[j][e];
-            const bool keep = (c0 + e < n) & ((v > Tf) | ((v == Tf) & (c0 + e <= tie_col)));
-            sel |= (keep ? 1u : 0u) << (4 * j + e);
-        }
-    }
+        for (int e = 0; e < 4; ++e) sel |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << (4 * j + e);
     static_assert(kStageGroups == kChunk, "one ranking round covers the row");
     int offs[kChunk];
     chunk_ranks(sh, sel, offs);

@@ -361,7 +361,10 @@ def make_logits(rows: int, width: int, ctx: Sequence[int], seed: int, kind: str 
 
     ``kind``: "normal" (distinct with high probability), "ints" (small integers,
     many exact ties), "const" (every visible value equal), "zeros" (a mix of
-    +0.0 and -0.0), "relu" (many exact zeros, like summed ReLU outputs).
+    +0.0 and -0.0), "relu" (many exact zeros, like summed ReLU outputs),
+    "offset" (values in [30000, 30000.49] plus seven distinct larger ones per
+    row, 30000.5 + 0.01 i: a range about 50,000 times narrower than its
+    largest value).
     ``tail`` fills ``[ctx, width)``: "neginf" or "nan".
     """
     rng = np.random.default_rng(seed)
@@ -377,6 +380,12 @@ def make_logits(rows: int, width: int, ctx: Sequence[int], seed: int, kind: str 
         x[:, ::7] = np.float32(1.5)
     elif kind == "relu":
         x = np.maximum(rng.standard_normal((rows, width), dtype=np.float32), np.float32(0.0))
+    elif kind == "offset":
+        x = (np.float32(30000.0) + np.float32(0.49) * rng.random((rows, width), dtype=np.float32)).astype(np.float32)
+        for r, c in enumerate(np.asarray(ctx, dtype=np.int64).reshape(rows)):
+            c = int(min(max(c, 0), width))
+            cols = rng.permutation(c)[:7]
+            x[r, cols] = (np.float32(30000.5) + np.float32(0.01) * np.arange(len(cols), dtype=np.float32)).astype(np.float32)
     else:
         raise ValueError(kind)
     fillv = np.float32(-np.inf) if tail == "neginf" else np.float32(np.nan)

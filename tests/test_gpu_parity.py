@@ -461,7 +461,7 @@ def test_empty_inputs():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", sorted(TOPK_PATHS))
-@pytest.mark.parametrize("kind", ["normal", "ints", "const", "zeros", "relu"])
+@pytest.mark.parametrize("kind", ["normal", "ints", "const", "zeros", "relu", "offset"])
 @pytest.mark.parametrize("k", [1, 7, 256, 2048])
 def test_topk_distributions(kind, k, path):
     W = 9000
