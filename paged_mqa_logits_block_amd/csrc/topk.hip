@@ -686,7 +686,7 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             const bool is_kth = l < nc && rank == need - 1;
             if (is_kth) sh.thr_key = mk;
             // a key equal to the k-th at a later column would be dropped
-            const int kl = __builtin_ctzll(ballot(is_kth));
+            const int kl = __builtin_ctzll(ballot(is_kth) | (1ull << 63));  // defined for an empty mask
             const uint32_t tk = (uint32_t)readlane((int)mk, kl);
             const int tc = readlane(mc, kl);
             const bool cut = ballot(l < nc && mk == tk && mc > tc) != 0ull;
