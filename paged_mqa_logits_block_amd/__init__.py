@@ -183,10 +183,23 @@ def topk_workspace_bytes(num_rows: int, width: int, k: int) -> int:
     return int(lib.qsa_topk_workspace_bytes(int(num_rows), int(width), int(k)))
 
 
-def _workspace(workspace, R: int, width: int, k: int, device):
+def _torch_stream(stream):
+    """The torch stream object for a `stream` argument (None: the current one)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _workspace(workspace, R: int, width: int, k: int, device, stream=None):
     """(tensor or None, pointer, bytes) for qsa_topk's workspace argument:
     "auto" allocates what the shape uses (nothing when it uses none), None
-    passes NULL (one workgroup per row), a uint8 device tensor is passed as is."""
+    passes NULL (one workgroup per row), a uint8 device tensor is passed as is.
+    An "auto" workspace is marked as in use on the launch stream, so the caching
+    allocator does not hand its memory to other work before the kernels that use
+    it have run, even after the last Python reference is gone."""
     import torch
     if workspace is None:
         return None, None, 0
@@ -196,6 +209,7 @@ def _workspace(workspace, R: int, width: int, k: int, device):
         if nbytes == 0:
             return None, None, 0
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace.record_stream(_torch_stream(stream))
     _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
     return workspace, workspace.data_ptr(), int(workspace.numel() * workspace.element_size())
 
@@ -217,7 +231,7 @@ def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, wor
     _require(out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (R, k),
              "out must be contiguous int32 [R, k]")
     stride = int(logits.stride(0)) if R > 0 else width
-    ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device)
+    ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device, stream)
     args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), ws_ptr, ws_bytes,
             _stream(stream))
     if events is None:
@@ -281,7 +295,7 @@ class PreparedTopk:
         R = int(logits.shape[0])
         width = int(logits.shape[1]) if width is None else int(width)
         stride = int(logits.stride(0)) if R > 0 else width
-        ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device)
+        ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device, stream)
         self._keep = (logits, ctx_lens, out, ws)
         self.workspace = ws
         self._args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), ws_ptr, ws_bytes,

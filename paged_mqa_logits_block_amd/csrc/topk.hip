@@ -448,8 +448,13 @@ __device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t km
     // with no finite value at all, a = 0 and ~b = ~0: the map is never used
     const float vmax = key_value(a), vmin = key_value(~b);
     const float span = vmax - vmin;
-    const bool usable = a != 0u && span > 0.0f && __builtin_isfinite(span);
-    return RowRange{vmax, usable ? (float)(kBins - 3) / span : 0.0f, c == 0u};
+    // a span narrower than about 6e-36 makes the scale (and the register path's
+    // offset vmax * scale) overflow; then one bucket holds the whole row, which
+    // keeps every later step exact
+    const float scale = (float)(kBins - 3) / span;
+    const bool usable = a != 0u && span > 0.0f && __builtin_isfinite(span) && __builtin_isfinite(scale) &&
+                        __builtin_isfinite(vmax * scale);
+    return RowRange{vmax, usable ? scale : 0.0f, c == 0u};
 }
 
 // running finite range and non-finite flag over one visible value
@@ -670,6 +675,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     }
     __syncthreads();
     const int nc = sh.ncand;  // == cnt: the same test as the histogram's
+    if (nc != cnt) {  // never expected; uniform (read after the barrier)
+        __syncthreads();
+        return false;
+    }
 
     // ---- the k-th pair (T, Ct) -------------------------------------------
     uint32_t T;
@@ -923,8 +932,9 @@ struct RangeBucketer {
 // a degenerate range maps everything to bucket 1.
 __device__ __forceinline__ RangeBucketer make_range(float vmax, float vmin, int nb) {
     const float span = vmax - vmin;
-    const bool usable = span > 0.0f && __builtin_isfinite(span);
-    return RangeBucketer{vmax, usable ? (float)(nb - 3) / span : 0.0f, (float)(nb - 3)};
+    const float scale = (float)(nb - 3) / span;
+    const bool usable = span > 0.0f && __builtin_isfinite(span) && __builtin_isfinite(scale);
+    return RangeBucketer{vmax, usable ? scale : 0.0f, (float)(nb - 3)};
 }
 
 // unsigned max over the kWaves per-wave partials (one LDS read per wave)

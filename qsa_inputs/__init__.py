@@ -364,7 +364,8 @@ def make_logits(rows: int, width: int, ctx: Sequence[int], seed: int, kind: str 
     +0.0 and -0.0), "relu" (many exact zeros, like summed ReLU outputs),
     "offset" (values in [30000, 30000.49] plus seven distinct larger ones per
     row, 30000.5 + 0.01 i: a range about 50,000 times narrower than its
-    largest value).
+    largest value), "tiny" (normal floats within 4,096 ulp of 1e-36: a range
+    below 1e-39, too narrow for 2,048 buckets of float32 width).
     ``tail`` fills ``[ctx, width)``: "neginf" or "nan".
     """
     rng = np.random.default_rng(seed)
@@ -386,6 +387,9 @@ def make_logits(rows: int, width: int, ctx: Sequence[int], seed: int, kind: str 
             c = int(min(max(c, 0), width))
             cols = rng.permutation(c)[:7]
             x[r, cols] = (np.float32(30000.5) + np.float32(0.01) * np.arange(len(cols), dtype=np.float32)).astype(np.float32)
+    elif kind == "tiny":
+        base = np.array([1e-36], dtype=np.float32).view(np.uint32)[0]
+        x = (base + rng.integers(0, 4096, size=(rows, width)).astype(np.uint32)).view(np.float32)
     else:
         raise ValueError(kind)
     fillv = np.float32(-np.inf) if tail == "neginf" else np.float32(np.nan)

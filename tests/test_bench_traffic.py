@@ -53,3 +53,42 @@ def test_source_hash_ignores_comments_only():
     code = "int a; // note\n/* block\n comment */\nint b;   \n\n"
     assert bench._code_only(code) == bench._code_only("int a;\nint b;") == "int a;\nint b;"
     assert bench._code_only("int a = 1;") != bench._code_only("int a = 2;")
+
+
+def test_write_traffic_topk_sums_its_kernels(tmp_path, monkeypatch):
+    """The split selection runs two kernels per call: their per-dispatch means
+    add up to the call's bytes, under the workload's ":topk" entry."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    win = "void qsa::(anonymous namespace)::topk_window_kernel<2>(qsa::TopkArgs)"
+    res = "void qsa::(anonymous namespace)::topk_resolve_kernel<2>(qsa::TopkArgs)"
+    score = "void qsa::(anonymous namespace)::paged_logits_kernel<0, 4, 1, 4>(qsa::LogitsArgs)"
+    write_csv(tmp_path / "cf", "FETCH_SIZE", [("copy", 524288.0)])
+    write_csv(tmp_path / "cw", "WRITE_SIZE", [("copy", 1048576.0)])
+    write_csv(tmp_path / "f", "FETCH_SIZE", [(score, 999.0), (win, 10.0), (res, 4.0), (win, 30.0), (res, 8.0)])
+    write_csv(tmp_path / "w", "WRITE_SIZE", [(score, 99.0), (win, 1.0), (res, 2.0), (win, 3.0), (res, 2.0)])
+    dirs = [str(tmp_path / d) for d in ("f", "w", "cf", "cw")]
+    bench.write_traffic("decode_verify", "topk", dirs, 1024)
+    t = json.load(open(tmp_path / "traffic.json"))["decode_verify:topk"]
+    assert t["fetch_bytes"] == (20 + 6) * 1024 * 2
+    assert t["write_bytes"] == (2 + 2) * 1024
+    assert t["dispatches"] == 2
+    assert "topk_window_kernel<2>" in t["kernel"] and "topk_resolve_kernel<2>" in t["kernel"]
+    assert bench.measured_traffic("decode_verify", "topk") == t["bytes_per_launch"]
+    assert bench.measured_traffic("decode_verify", "paged_logits_kernel") is None
+
+
+def test_write_mfma_busy_fraction(tmp_path, monkeypatch):
+    """MFMA busy cycles over 1,024 SIMDs x one XCD's share of GRBM_GUI_ACTIVE."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    k = "prefill_logits_kernel"
+    full = "void qsa::(anonymous namespace)::prefill_logits_kernel<0, false, 8>(qsa::LogitsArgs)"
+    folder = tmp_path / "m"
+    os.makedirs(folder / "host", exist_ok=True)
+    with open(folder / "host" / "run_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=FIELDS)
+        wr.writeheader()
+        for i, (c, v) in enumerate([("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 500.0), ("GRBM_GUI_ACTIVE", 8 * 1000.0),
+                                    ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 300.0), ("GRBM_GUI_ACTIVE", 8 * 1000.0)]):
+            wr.writerow({"Dispatch_Id": i // 2, "Kernel_Name": full, "Counter_Name": c, "Counter_Value": v})
+    bench.write_mfma("prefill_chunk", k, str(folder))
+    assert bench.measured_mfma_busy("prefill_chunk", k) == 0.4

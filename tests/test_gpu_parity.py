@@ -14,7 +14,7 @@ import pytest
 import oracle
 import qsa_inputs
 from gpu_helpers import (TOPK_PATHS, qsa, assert_logits_match, assert_topk_banded, assert_topk_exact,
-                         gpu_logits, gpu_topk, topk_tol)
+                         gpu_logits, gpu_topk)
 from qsa_inputs.device import to_device
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +47,13 @@ def run_logits(inp, **kw):
 # the five workloads
 # ---------------------------------------------------------------------------
 
-SAMPLED_ROWS = {"prefill_chunk": [0, 1, 2, 3, 1000, 4095, 4096, 8191, 12000, 16380, 16381, 16382, 16383]}
+def _prefill_sample_rows(n=16384):
+    """One whole 128-row tile of the prefill scoring kernel, every 16th row after
+    it (other tiles, both halves of each consumer wave's rows), and the last."""
+    return sorted(set(range(128)) | set(range(128, n, 16)) | {n - 1})
+
+
+SAMPLED_ROWS = {"prefill_chunk": _prefill_sample_rows()}
 SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 
 
@@ -57,29 +63,33 @@ SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 def test_config_logits_and_topk(name):
     inp = qsa_inputs.make_config(name, poison=True)
     rows = SAMPLED_ROWS.get(name)
-    say(name, "rows", inp.num_rows, "width", inp.width, "H", inp.num_heads, inp.dtype, inp.layout)
+    say(name, "rows", inp.num_rows, "width", inp.width, "H", inp.num_heads, inp.dtype, inp.layout,
+        "compared rows", inp.num_rows if rows is None else len(rows))
     dev, g = run_logits(inp)
     sel = list(range(inp.num_rows)) if rows is None else rows
     o = oracle.paged_logits(inp, rows=sel)
     gl = g[torch.tensor(sel, device="cuda")].cpu().numpy()
-    assert_logits_match(gl, o, inp, sel, label=name)
+    tols = assert_logits_match(gl, o, inp, sel, label=name)
 
-    # top-k on the GPU's own logits, end to end, against the oracle's selection
+    # top-k on the GPU's own logits (all rows in one call, as the benchmark
+    # runs it), end to end, against the oracle's selection
     gi = gpu_topk(g, dev.ctx_lens, inp.topk)[torch.tensor(sel, device="cuda")].cpu().numpy()
     o32 = o.astype(np.float32)
     oi = oracle.topk(o32, inp.ctx_lens[sel], inp.topk)
-    assert_topk_banded(gi, oi, o, topk_tol(inp), label=name)
+    assert_topk_banded(gi, oi, o, tols, label=name)
 
-    # top-k on identical logits (the oracle's, uploaded): exact
+    # top-k on identical logits (the oracle's, uploaded; every compared row in
+    # one call): exact, on both selection paths where the shape has two
     lt = torch.from_numpy(np.ascontiguousarray(o32)).cuda()
     ct = torch.from_numpy(inp.ctx_lens[sel].astype(np.int32)).cuda()
-    gi2 = gpu_topk(lt, ct, inp.topk).cpu().numpy()
-    assert_topk_exact(gi2, oi, label=name)
-    # ascending column order, -1 padding after the selection
-    for r in range(gi2.shape[0]):
-        v = gi2[r][gi2[r] >= 0]
-        assert np.all(np.diff(v) > 0)
-        assert np.all(gi2[r][len(v):] == -1)
+    for path, ws in TOPK_PATHS.items():
+        gi2 = gpu_topk(lt, ct, inp.topk, workspace=ws).cpu().numpy()
+        assert_topk_exact(gi2, oi, label=f"{name} {path}")
+        # ascending column order, -1 padding after the selection
+        for r in range(gi2.shape[0]):
+            v = gi2[r][gi2[r] >= 0]
+            assert np.all(np.diff(v) > 0)
+            assert np.all(gi2[r][len(v):] == -1)
 
 
 # ---------------------------------------------------------------------------
@@ -250,10 +260,21 @@ def test_head_dim_64(dtype, layout, H, B, req_rows):
     """Head dim 64 (the per-tile kernel for every shape): zero K steps for
     bf16/fp16, zero lane groups in the fp8 MFMA; 4-row requests and many heads
     that take other kernels at D = 128; block sizes with the per-column gather."""
-    if layout == "copacked_shuffled" and B % 16:
-        pytest.skip("the preshuffled layout needs blocks of a multiple of 16")
     R = sum(req_rows)
     ctx = [[1, 15, 16, 17, 64, 65, 1000, 1999, 2000, 7, 33, 500][i % 12] for i in range(R)]
+    if layout == "copacked_shuffled" and B % 16:
+        # the preshuffled layout is defined for blocks of a multiple of 16
+        # columns: the call is refused before any launch
+        m = qsa()
+        inp = qsa_inputs.build(name="d64", seed=300 + H + B, req_rows=req_rows, ctx_rows=ctx, num_heads=H,
+                               head_dim=64, block_size=B, dtype=dtype, layout="copacked", weights=True)
+        dev = to_device(inp)
+        say("head dim 64 refused", dtype, layout, "H", H, "B", B)
+        with pytest.raises(m.QsaError) as e:
+            m.paged_logits(dev.q, dev.kcache, dev.block_table, dev.ctx_lens, dev.row_to_req, width=dev.width,
+                           block_size=B, w=dev.w, layout=m.KV_COPACKED_SHUFFLED)
+        assert e.value.status == m.E_UNSUPPORTED
+        return
     inp = qsa_inputs.build(name="d64", seed=300 + H + B, req_rows=req_rows, ctx_rows=ctx, num_heads=H,
                            head_dim=64, block_size=B, dtype=dtype, layout=layout, weights=True, poison=True)
     say("head dim 64", dtype, layout, "H", H, "B", B)
@@ -461,7 +482,7 @@ def test_empty_inputs():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", sorted(TOPK_PATHS))
-@pytest.mark.parametrize("kind", ["normal", "ints", "const", "zeros", "relu", "offset"])
+@pytest.mark.parametrize("kind", ["normal", "ints", "const", "zeros", "relu", "offset", "tiny"])
 @pytest.mark.parametrize("k", [1, 7, 256, 2048])
 def test_topk_distributions(kind, k, path):
     W = 9000
@@ -684,3 +705,117 @@ def test_graph_capture_replay(name):
         lg2()  # eager work on other inputs between the replays
         tk2()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("rows", [3, 200])
+def test_topk_range_too_narrow_for_buckets(rows):
+    """Rows whose values all lie within 4,096 ulp of 1e-36 (a range below 1e-39):
+    2,048 buckets over that range would need a scale beyond float32, so the
+    whole row shares one bucket and the members are ranked exactly.  Visible
+    counts just above k (at most 2,048: the register path ranks them from its
+    member list) and far above it (the list overflows: the staged path)."""
+    W, k = 6000, 300
+    ctx = np.array([k + 1, 1000, 2048, 5999, W, 2049][: max(rows, 3)] * (rows // 3 + 1))[:rows]
+    x = qsa_inputs.make_logits(rows, W, ctx, seed=rows, kind="tiny")
+    say("topk tiny range", rows)
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    oi = oracle.topk(x, ctx, k)
+    for path, ws in TOPK_PATHS.items():
+        gi = gpu_topk(xt, ct, k, workspace=ws).cpu().numpy()
+        assert_topk_exact(gi, oi, label=f"tiny range {path}")
+
+
+def test_topk_side_stream_auto_workspace():
+    """topk(..., stream=s) with an automatic workspace: the workspace stays
+    reserved for s until the selection has run there, so memory allocated and
+    written on the current stream right after the call does not overlap it."""
+    m = qsa()
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep is not available")
+    W, k, rows = 30000, 2048, 36
+    rng = np.random.default_rng(41)
+    ctx = rng.integers(k + 1, W + 1, size=rows).astype(np.int32)
+    x = qsa_inputs.make_logits(rows, W, ctx, seed=41, kind="normal")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx).cuda()
+    nbytes = m.topk_workspace_bytes(rows, W, k)
+    assert nbytes > 0
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    say("topk side stream workspace")
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(2_000_000)  # holds s for about a millisecond
+    out = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    m.topk(xt, ct, k, out=out, stream=s)
+    # current stream: allocate the workspace's size and fill it at once
+    filler = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    filler.fill_(0x5A)
+    torch.cuda.synchronize()
+    assert bool(torch.all(filler == 0x5A)), "the selection wrote into memory handed out after the call"
+    assert_topk_exact(out.cpu().numpy(), oracle.topk(x, ctx, k), label="side stream")
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_verify", "fp8_paged"])
+def test_graph_replay_new_inputs_in_place(name):
+    """vLLM PR #62589, Validation: capture once, then replay with new queries
+    and visible lengths written into the captured buffers.  Each replay equals
+    the oracle on the new inputs (logits to the gate, top-k exact on the replay's
+    own logits) and an eager call on the same buffers bit for bit."""
+    import dataclasses
+
+    m = qsa()
+    inp = qsa_inputs.make_config(name)
+    dev = to_device(inp)
+    R, W, k = inp.num_rows, inp.width, inp.topk
+    s = torch.cuda.Stream()
+    out = torch.empty((R, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    lg = m.PreparedLogits(dev.q, dev.kcache, dev.block_table, dev.ctx_lens, dev.row_to_req, out, width=W,
+                          block_size=dev.block_size, w=dev.w, kscale=dev.kscale, layout=dev.layout, stream=s)
+    tk = m.PreparedTopk(out, dev.ctx_lens, k, idx, stream=s)
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    say("graph replay, new inputs in place", name)
+    with torch.cuda.stream(s):
+        lg()
+        tk()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lg()
+        tk()
+    torch.cuda.synchronize()
+    for trial in range(3):
+        rng = np.random.default_rng(5000 + trial)
+        qf = rng.standard_normal(inp.q.shape).astype(np.float32)
+        new_q = (qsa_inputs.f32_to_e4m3fn_codes(qf) if inp.dtype == "fp8"
+                 else qsa_inputs.f32_to_bf16_bits(qf))
+        # each row sees at most its request's keys
+        cap = np.minimum(np.asarray(inp.kv_lens)[inp.row_to_req], W).astype(np.int64)
+        new_ctx = (rng.random(R) * (cap + 1)).astype(np.int32)
+        new_ctx[0], new_ctx[-1] = cap[0], max(0, min(int(cap[-1]), k - 1))
+        inp2 = dataclasses.replace(inp, q=new_q, ctx_lens=new_ctx)
+        dev2 = to_device(inp2)
+        dev.q.copy_(dev2.q)
+        dev.ctx_lens.copy_(dev2.ctx_lens)
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        x = out.cpu().numpy()
+        gi = idx.cpu().numpy()
+        o = oracle.paged_logits(inp2)
+        assert_logits_match(x, o, inp2, label=f"{name} replay {trial}")
+        assert_topk_exact(gi, oracle.topk(x, new_ctx, k), label=f"{name} replay {trial}")
+        ref, ref_idx = out.clone(), idx.clone()
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            lg()
+            tk()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(idx, ref_idx), f"{name} replay {trial}: eager differs"
