@@ -156,20 +156,34 @@ QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const v
                                   const float *out, const qsa_logits_shape *shape);
 
 /*
- * qsa_topk -- per row r, the k columns of [0, n_r), n_r = clamp(ctx_lens[r], 0,
- * width), with the largest logits; equal logits (+0 and -0 are equal) are broken
- * toward the lower column.  Rows with n_r <= k keep all of [0, n_r).
+ * qsa_topk -- per row r, the k columns of its candidate range with the largest
+ * logits; equal logits (+0 and -0 are equal) are broken toward the lower
+ * column.  Rows with n_r <= k keep their whole range.
  *
- *   logits   [num_rows][logits_stride] f32 (the buffer holds num_rows *
- *            logits_stride floats); only columns [0, n_r) decide the result
- *            (reads are rounded up to a multiple of 4 columns).
- *   ctx_lens [num_rows] int32.
- *   idx_out  [num_rows][k] int32: the selected columns in ascending order, then
- *            -1 in slots [min(k, n_r), k).  The order is part of this
- *            implementation, not of the selection's definition (a set).
+ * Candidate range (vLLM PR #62589, "Details": top-k reads only the visible
+ * columns; sglang PR #48649, "Accuracy Tests": the top-k takes per-row starts
+ * and context lengths, and rows that fit in k keep everything):
+ *   s_r = clamp(row_starts[r], 0, width)  (0 when row_starts is NULL),
+ *   n_r = clamp(ctx_lens[r], 0, width - s_r),
+ * the columns [s_r, s_r + n_r) of row r.  An index is reported as the offset
+ * of its column from s_r, in [0, n_r): a row's result does not depend on where
+ * its range sits in the buffer.
  *
- * Device precondition: no NaN inside [0, n_r) (a NaN ranks by its bit pattern:
- * above +inf when its sign is clear, below -inf when set).
+ *   logits     [num_rows][logits_stride] f32 (the buffer holds num_rows *
+ *              logits_stride floats); only the candidate range decides the
+ *              result (reads are widened to whole 16-byte groups inside the
+ *              row's stride).
+ *   ctx_lens   [num_rows] int32: candidate count per row.
+ *   row_starts [num_rows] int32, or NULL: first candidate column per row.
+ *              Starts that are multiples of 4 take the same paths as no
+ *              starts; other starts are exact but use the slower full-row
+ *              selection for rows longer than k.
+ *   idx_out    [num_rows][k] int32: the selected offsets in ascending order,
+ *              then -1 in slots [min(k, n_r), k).  The order is part of this
+ *              implementation, not of the selection's definition (a set).
+ *
+ * Device precondition: no NaN inside a candidate range (a NaN ranks by its bit
+ * pattern: above +inf when its sign is clear, below -inf when set).
  *
  *   workspace  device scratch owned by the caller, or NULL.  With NULL every
  *              row is selected by one workgroup.  Otherwise it must hold at
@@ -186,8 +200,8 @@ QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const v
  * Alignment (else QSA_E_ALIGN): logits 16-byte aligned, logits_stride % 4 == 0.
  */
 QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
-                            int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out,
-                            void *workspace, int64_t workspace_bytes, void *stream);
+                            const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
+                            int32_t *idx_out, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Bytes of workspace qsa_topk uses for this shape; 0 when every row is selected
  * by one workgroup whatever the workspace.  Host-only, no HIP call; k does not
@@ -198,14 +212,35 @@ QSA_API int64_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t width, int32_
  * qsa_paged_logits_timed): start_event at the start of the first kernel,
  * stop_event at the end of the last. */
 QSA_API qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
-                                  int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out,
-                                  void *workspace, int64_t workspace_bytes, void *stream,
+                                  const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
+                                  int32_t *idx_out, void *workspace, int64_t workspace_bytes, void *stream,
                                   void *start_event, void *stop_event);
 
 /* Validation of qsa_topk's host-visible arguments only: no HIP call, no launch. */
 QSA_API qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
-                                  int32_t num_rows, int32_t width, int32_t k, const int32_t *idx_out,
-                                  const void *workspace, int64_t workspace_bytes);
+                                  const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
+                                  const int32_t *idx_out, const void *workspace, int64_t workspace_bytes);
+
+/*
+ * qsa_expand -- the step after the selection: each selected compressed column
+ * becomes the key tokens it stands for.  The pages time a full selection as
+ * "score + top-k + expand" with a compression ratio of 4 (vLLM PR #62589,
+ * "Performance" and the MI355X comment) without defining the step; this is the
+ * plain reading: compressed column c covers tokens [c * ratio, c * ratio + ratio).
+ *
+ *   idx         [num_rows][k] int32 selected columns (qsa_topk's output; -1 is
+ *               padding).
+ *   token_lens  [num_rows] int32 tokens per row, or NULL for no bound.
+ *   tokens_out  [num_rows][k * ratio] int32: slot p * ratio + j holds
+ *               idx[r][p] * ratio + j when idx[r][p] >= 0 and that token is below
+ *               token_lens[r] (and fits in int32), else -1.  Ascending columns
+ *               give ascending tokens.
+ *
+ * Errors: QSA_E_INVALID for null pointers with num_rows > 0, num_rows < 0,
+ * k < 1 or ratio < 1; QSA_E_RANGE when k * ratio > 2^24.
+ */
+QSA_API qsa_status qsa_expand(const int32_t *idx, int32_t num_rows, int32_t k, int32_t ratio,
+                              const int32_t *token_lens, int32_t *tokens_out, void *stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). Owned by the
  * library; valid until the thread's next call. */

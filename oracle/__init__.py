@@ -58,9 +58,12 @@ def load(path: Optional[str] = None):
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
     lib.ora_paged_logits.restype = ctypes.c_int
-    lib.ora_topk.argtypes = [ctypes.c_void_p, ctypes.c_int64, i32p, ctypes.c_int, ctypes.c_int,
-                             ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+    lib.ora_topk.argtypes = [ctypes.c_void_p, ctypes.c_int64, i32p, ctypes.c_void_p, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
     lib.ora_topk.restype = ctypes.c_int
+    lib.ora_expand.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.ora_expand.restype = ctypes.c_int
     lib.ora_max_threads.argtypes = []
     lib.ora_max_threads.restype = ctypes.c_int
     if path is None:
@@ -133,16 +136,31 @@ def paged_logits(inp, rows: Optional[Sequence[int]] = None, threads: int = 0,
     return out
 
 
-def topk(logits: np.ndarray, ctx_lens, k: int, threads: int = 0, lib=None) -> np.ndarray:
-    """int32 ``[R, k]`` column indices; -1 past min(k, ctx)."""
+def topk(logits: np.ndarray, ctx_lens, k: int, threads: int = 0, lib=None, row_starts=None) -> np.ndarray:
+    """int32 ``[R, k]`` offsets from each row's start (0 without ``row_starts``);
+    -1 past min(k, candidates)."""
     lib = lib or load()
     x = np.ascontiguousarray(logits, dtype=np.float32)
     R, W = x.shape
     ctx = np.ascontiguousarray(np.asarray(ctx_lens).reshape(R), dtype=np.int32)
+    st = None if row_starts is None else np.ascontiguousarray(np.asarray(row_starts).reshape(R), dtype=np.int32)
     out = np.empty((R, k), dtype=np.int32)
-    st = lib.ora_topk(_ptr(x), W, _i32(ctx), R, W, int(k), _ptr(out), threads)
-    if st != 0:
-        raise OracleError(f"ora_topk status {st}")
+    status = lib.ora_topk(_ptr(x), W, _i32(ctx), _ptr(st), R, W, int(k), _ptr(out), threads)
+    if status != 0:
+        raise OracleError(f"ora_topk status {status}")
+    return out
+
+
+def expand(idx: np.ndarray, ratio: int, token_lens=None, lib=None) -> np.ndarray:
+    """int32 ``[R, k * ratio]`` tokens of the selected compressed columns."""
+    lib = lib or load()
+    i = np.ascontiguousarray(idx, dtype=np.int32)
+    R, k = i.shape
+    tl = None if token_lens is None else np.ascontiguousarray(np.asarray(token_lens).reshape(R), dtype=np.int32)
+    out = np.empty((R, k * int(ratio)), dtype=np.int32)
+    status = lib.ora_expand(_ptr(i), R, k, int(ratio), _ptr(tl), _ptr(out))
+    if status != 0:
+        raise OracleError(f"ora_expand status {status}")
     return out
 
 

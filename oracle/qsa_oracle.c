@@ -261,15 +261,19 @@ static int cand_cmp(const void *pa, const void *pb)
 }
 
 /*
- * Per row: the min(k, n) columns of [0, n), n = clamp(ctx[row], 0, width),
- * with the largest logits; among equal logits the lower column is kept.
- * Slots past min(k, n) hold -1.  Emitted in (value desc, column asc) order;
- * the contract is the set (vLLM PR #62589, Validation: compared as sets;
- * sglang PR #48649 test body: entries < 0 are padding).
- * Returns ORA_E_NAN when a NaN lies inside [0, n): a precondition violation.
+ * Per row: candidates are the n columns from the row's start s, with
+ * s = clamp(row_starts[row], 0, width) (0 without starts) and
+ * n = clamp(ctx[row], 0, width - s); the min(k, n) with the largest logits are
+ * kept, among equal logits the lower column.  Each is reported as its offset
+ * from s (sglang PR #48649 test body: the top-k takes per-row starts and
+ * context lengths).  Slots past min(k, n) hold -1.  Emitted in (value desc,
+ * column asc) order; the contract is the set (vLLM PR #62589, Validation:
+ * compared as sets; the same test body: entries < 0 are padding).
+ * Returns ORA_E_NAN when a NaN lies inside a candidate range: a precondition
+ * violation.
  */
-int ora_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int num_rows,
-             int width, int k, int32_t *idx_out, int n_threads)
+int ora_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, const int32_t *row_starts,
+             int num_rows, int width, int k, int32_t *idx_out, int n_threads)
 {
     if (!logits || !ctx_lens || !idx_out || num_rows < 0 || width < 0 || k < 1 ||
         stride < width)
@@ -281,18 +285,23 @@ int ora_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int n
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
     for (int row = 0; row < num_rows; ++row) {
+        int64_t s = row_starts ? row_starts[row] : 0;
+        if (s < 0)
+            s = 0;
+        if (s > width)
+            s = width;
         int64_t n = ctx_lens[row];
         if (n < 0)
             n = 0;
-        if (n > width)
-            n = width;
+        if (n > width - s)
+            n = width - s;
         int32_t *o = idx_out + (int64_t)row * k;
         ora_cand *c = (ora_cand *)malloc(sizeof(ora_cand) * (size_t)(n > 0 ? n : 1));
         if (!c) {
             status = ORA_E_ARG;
             continue;
         }
-        const float *x = logits + (int64_t)row * stride;
+        const float *x = logits + (int64_t)row * stride + s;
         int bad = 0;
         for (int64_t j = 0; j < n; ++j) {
             c[j].v = x[j];
@@ -316,6 +325,35 @@ int ora_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int n
         free(c);
     }
     return status;
+}
+
+/*
+ * Expand: the tokens of each selected compressed column.  The pages time the
+ * full selection as score + top-k + expand with compression ratio 4 (vLLM
+ * PR #62589, Performance table heading and the MI355X comment) but do not
+ * define the step; the reading taken: column c stands for the `ratio` tokens
+ * c * ratio + j, j = 0 .. ratio - 1.  out[row][p * ratio + j] is that token for
+ * the p-th selected column when the column is not padding (>= 0) and the token
+ * lies below the row's token count (no bound without token_lens) and fits in
+ * int32; -1 otherwise.
+ */
+int ora_expand(const int32_t *idx, int num_rows, int k, int ratio, const int32_t *token_lens,
+               int32_t *out)
+{
+    if (!idx || !out || num_rows < 0 || k < 1 || ratio < 1)
+        return ORA_E_ARG;
+    for (int row = 0; row < num_rows; ++row) {
+        for (int p = 0; p < k; ++p) {
+            int32_t c = idx[(int64_t)row * k + p];
+            for (int j = 0; j < ratio; ++j) {
+                int64_t tok = (int64_t)c * ratio + j;
+                int keep = c >= 0 && tok <= INT32_MAX &&
+                           (!token_lens || tok < (int64_t)token_lens[row]);
+                out[((int64_t)row * k + p) * ratio + j] = keep ? (int32_t)tok : -1;
+            }
+        }
+    }
+    return ORA_OK;
 }
 
 int ora_max_threads(void)

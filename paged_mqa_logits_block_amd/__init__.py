@@ -25,8 +25,8 @@ BF16, FP8_E4M3FN, FP16 = 0, 1, 2
 KV_PAGED, KV_COPACKED, KV_COPACKED_SHUFFLED = 0, 1, 2
 
 EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
-            "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_last_error",
-            "qsa_version")
+            "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_expand",
+            "qsa_last_error", "qsa_version")
 
 
 class QsaError(RuntimeError):
@@ -65,12 +65,14 @@ def _load():
     lib.qsa_paged_logits_timed.restype = ctypes.c_int
     lib.qsa_paged_logits_check.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp]
     lib.qsa_paged_logits_check.restype = ctypes.c_int
-    lib.qsa_topk.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, i64, vp]
+    lib.qsa_topk.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp, i64, vp]
     lib.qsa_topk.restype = ctypes.c_int
-    lib.qsa_topk_timed.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, i64, vp, vp, vp]
+    lib.qsa_topk_timed.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp, i64, vp, vp, vp]
     lib.qsa_topk_timed.restype = ctypes.c_int
-    lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32, i32, i32, i32p, vp, i64]
+    lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp, i64]
     lib.qsa_topk_check.restype = ctypes.c_int
+    lib.qsa_expand.argtypes = [i32p, i32, i32, i32, i32p, i32p, vp]
+    lib.qsa_expand.restype = ctypes.c_int
     lib.qsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.qsa_topk_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_last_error.argtypes = []
@@ -214,9 +216,16 @@ def _workspace(workspace, R: int, width: int, k: int, device, stream=None):
     return workspace, workspace.data_ptr(), int(workspace.numel() * workspace.element_size())
 
 
-def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, workspace="auto",
-         stream=None, events=None):
-    """``qsa_topk``: int32 ``[R, k]`` selected columns, ascending, -1 padded.
+def _check_rows_i32(name, t, R):
+    import torch
+    _require(t.is_cuda and t.dtype == torch.int32 and t.is_contiguous() and int(t.numel()) == R,
+             f"{name} must be a contiguous int32 device tensor with one entry per row")
+
+
+def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, row_starts=None, out=None,
+         workspace="auto", stream=None, events=None):
+    """``qsa_topk``: int32 ``[R, k]`` selected offsets from each row's start
+    (``row_starts``, default 0), ascending, -1 padded.
     ``workspace``: "auto" (allocate the scratch the shape uses), None (NULL:
     one workgroup per row) or a uint8 device tensor."""
     import torch
@@ -225,6 +234,8 @@ def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, wor
              "logits must be f32 [R, >=width] with unit column stride")
     _require(ctx_lens.dtype == torch.int32 and ctx_lens.is_contiguous(), "ctx_lens must be contiguous int32")
     R = int(logits.shape[0])
+    if row_starts is not None:
+        _check_rows_i32("row_starts", row_starts, R)
     width = int(logits.shape[1]) if width is None else int(width)
     if out is None:
         out = torch.empty((R, k), dtype=torch.int32, device=logits.device)
@@ -232,13 +243,31 @@ def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, out=None, wor
              "out must be contiguous int32 [R, k]")
     stride = int(logits.stride(0)) if R > 0 else width
     ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device, stream)
-    args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), ws_ptr, ws_bytes,
-            _stream(stream))
+    args = (_ptr(logits), stride, _ptr(ctx_lens), _ptr(row_starts), R, width, int(k), _ptr(out), ws_ptr,
+            ws_bytes, _stream(stream))
     if events is None:
         st = lib.qsa_topk(*args)
     else:
         st = lib.qsa_topk_timed(*args, _event(events[0]), _event(events[1]))
     _raise_on(st)
+    return out
+
+
+def expand(idx, ratio: int, *, token_lens=None, out=None, stream=None):
+    """``qsa_expand``: int32 ``[R, k * ratio]`` tokens of the selected compressed
+    columns (column c covers tokens c * ratio .. c * ratio + ratio - 1), -1 for
+    padding and for tokens at or past ``token_lens``."""
+    import torch
+    _require(idx.is_cuda and idx.dtype == torch.int32 and idx.dim() == 2 and idx.is_contiguous(),
+             "idx must be a contiguous int32 [R, k] device tensor")
+    R, k = (int(x) for x in idx.shape)
+    if token_lens is not None:
+        _check_rows_i32("token_lens", token_lens, R)
+    if out is None:
+        out = torch.empty((R, k * int(ratio)), dtype=torch.int32, device=idx.device)
+    _require(out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (R, k * int(ratio)),
+             "out must be contiguous int32 [R, k * ratio]")
+    _raise_on(lib.qsa_expand(_ptr(idx), R, k, int(ratio), _ptr(token_lens), _ptr(out), _stream(stream)))
     return out
 
 
@@ -250,10 +279,10 @@ def paged_logits_check(q_ptr, w_ptr, kcache_ptr, kscale_ptr, bt_ptr, ctx_ptr, r2
 
 
 def topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr, workspace_ptr=None,
-               workspace_bytes=0) -> int:
+               workspace_bytes=0, row_starts_ptr=None) -> int:
     """Host-side validation only (``qsa_topk_check``); pointers are ints."""
-    return lib.qsa_topk_check(logits_ptr, stride, ctx_ptr, num_rows, width, k, out_ptr, workspace_ptr,
-                              workspace_bytes)
+    return lib.qsa_topk_check(logits_ptr, stride, ctx_ptr, row_starts_ptr, num_rows, width, k, out_ptr,
+                              workspace_ptr, workspace_bytes)
 
 
 class PreparedLogits:
@@ -290,17 +319,19 @@ class PreparedTopk:
     """A validated ``qsa_topk`` call on fixed tensors (see PreparedLogits); the
     workspace ("auto": allocated once here) is part of the prepared call."""
 
-    def __init__(self, logits, ctx_lens, k: int, out, *, width: Optional[int] = None, workspace="auto",
-                 stream=None):
+    def __init__(self, logits, ctx_lens, k: int, out, *, width: Optional[int] = None, row_starts=None,
+                 workspace="auto", stream=None):
         R = int(logits.shape[0])
         width = int(logits.shape[1]) if width is None else int(width)
         stride = int(logits.stride(0)) if R > 0 else width
+        if row_starts is not None:
+            _check_rows_i32("row_starts", row_starts, R)
         ws, ws_ptr, ws_bytes = _workspace(workspace, R, width, k, logits.device, stream)
-        self._keep = (logits, ctx_lens, out, ws)
+        self._keep = (logits, ctx_lens, row_starts, out, ws)
         self.workspace = ws
-        self._args = (_ptr(logits), stride, _ptr(ctx_lens), R, width, int(k), _ptr(out), ws_ptr, ws_bytes,
-                      _stream(stream))
-        _raise_on(lib.qsa_topk_check(*self._args[:9]))
+        self._args = (_ptr(logits), stride, _ptr(ctx_lens), _ptr(row_starts), R, width, int(k), _ptr(out), ws_ptr,
+                      ws_bytes, _stream(stream))
+        _raise_on(lib.qsa_topk_check(*self._args[:10]))
         self.out = out
 
     def __call__(self, events=None):

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqsaidx.so")
 SOURCES = ["api.hip", "logits.hip", "logits_decode.hip", "logits_looped.hip", "logits_mtp.hip",
-           "logits_prefill.hip", "topk.hip"]
+           "logits_prefill.hip", "topk.hip", "expand.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

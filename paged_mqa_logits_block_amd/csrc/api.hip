@@ -81,6 +81,8 @@ qsa_status check_logits(const void *q, const float *w, const void *kcache, const
     return ok();
 }
 
+// row_starts needs no host check: NULL means every start is 0, and any device
+// value is clamped to [0, width] by the kernels.
 qsa_status check_topk(const float *logits, int64_t stride, const int32_t *ctx_lens, int32_t num_rows,
                       int32_t width, int32_t k, const int32_t *idx_out, const void *workspace,
                       int64_t workspace_bytes) {
@@ -179,22 +181,24 @@ int64_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t width, int32_t k) {
     return qsa::topk_workspace_bytes(num_rows, width);
 }
 
-qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
-                          int32_t width, int32_t k, const int32_t *idx_out, const void *workspace,
-                          int64_t workspace_bytes) {
+qsa_status qsa_topk_check(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                          const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
+                          const int32_t *idx_out, const void *workspace, int64_t workspace_bytes) {
+    (void)row_starts;
     return check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, workspace, workspace_bytes);
 }
 
-qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
-                    int32_t width, int32_t k, int32_t *idx_out, void *workspace, int64_t workspace_bytes,
-                    void *stream) {
-    return qsa_topk_timed(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, workspace,
+qsa_status qsa_topk(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, const int32_t *row_starts,
+                    int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out, void *workspace,
+                    int64_t workspace_bytes, void *stream) {
+    return qsa_topk_timed(logits, logits_stride, ctx_lens, row_starts, num_rows, width, k, idx_out, workspace,
                           workspace_bytes, stream, nullptr, nullptr);
 }
 
-qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens, int32_t num_rows,
-                          int32_t width, int32_t k, int32_t *idx_out, void *workspace, int64_t workspace_bytes,
-                          void *stream, void *start_event, void *stop_event) {
+qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                          const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k, int32_t *idx_out,
+                          void *workspace, int64_t workspace_bytes, void *stream, void *start_event,
+                          void *stop_event) {
     qsa_status st = check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, workspace,
                                workspace_bytes);
     if (st != QSA_OK) return st;
@@ -203,6 +207,7 @@ qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int3
     a.logits = logits;
     a.stride = logits_stride;
     a.ctx_lens = ctx_lens;
+    a.row_starts = row_starts;
     a.num_rows = num_rows;
     a.width = width;
     a.k = k;
@@ -221,6 +226,21 @@ qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int3
     }
     hipError_t e = qsa::launch_topk(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
                                     static_cast<hipEvent_t>(stop_event));
+    if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+qsa_status qsa_expand(const int32_t *idx, int32_t num_rows, int32_t k, int32_t ratio, const int32_t *token_lens,
+                      int32_t *tokens_out, void *stream) {
+    if (num_rows < 0) return fail(QSA_E_INVALID, "num_rows = %d < 0", num_rows);
+    if (k < 1) return fail(QSA_E_INVALID, "k = %d < 1", k);
+    if (ratio < 1) return fail(QSA_E_INVALID, "ratio = %d < 1", ratio);
+    if ((int64_t)k * ratio > ((int64_t)1 << 24))
+        return fail(QSA_E_RANGE, "k * ratio = %lld > 2^24", (long long)k * ratio);
+    if (num_rows == 0) return ok();
+    if (!idx || !tokens_out) return fail(QSA_E_INVALID, "idx and tokens_out must be non-NULL");
+    qsa::ExpandArgs a = {idx, token_lens, tokens_out, num_rows, k, ratio};
+    hipError_t e = qsa::launch_expand(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }

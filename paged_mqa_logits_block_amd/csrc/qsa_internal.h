@@ -73,6 +73,7 @@ struct TopkArgs {
     const float *logits;
     int64_t stride;
     const int32_t *ctx_lens;
+    const int32_t *row_starts;  // first candidate column per row, or null (0)
     int32_t num_rows;
     int32_t width;
     int32_t k;
@@ -97,5 +98,17 @@ int topk_groups_for_width(int width);  // 1 if the width is supported, else 0
 TopkPlan plan_topk(int num_rows, int width);
 int64_t topk_workspace_bytes(int num_rows, int width);  // 0: no workspace used
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
+
+// Selected compressed columns -> tokens (qsa_expand).
+struct ExpandArgs {
+    const int32_t *idx;         // [num_rows][k]
+    const int32_t *token_lens;  // [num_rows] or null
+    int32_t *tokens_out;        // [num_rows][k * ratio]
+    int32_t num_rows;
+    int32_t k;
+    int32_t ratio;
+};
+
+hipError_t launch_expand(const ExpandArgs &a, hipStream_t s);
 
 }  // namespace qsa

@@ -2,7 +2,9 @@
 //
 // Selects, per row, the k columns of [0, n) with the largest logits, ties to
 // the lower column (+0 and -0 equal), and writes them in ascending column order
-// followed by -1 padding.  Rows with n <= k keep all of [0, n) (sglang
+// followed by -1 padding.  With row starts, a row's candidates are the n
+// columns from its start s, and the indices written are offsets from s (the
+// sglang PR #48649 test body passes per-row starts to its top-k).  Rows with n <= k keep all of [0, n) (sglang
 // PR #48649, Accuracy Tests: rows that fit in k need no selection); nothing past n
 // is used (vLLM PR #62589, Details and Validation).
 //
@@ -85,6 +87,41 @@ __device__ __forceinline__ f32x4 load4(const float *src, int i) {
     return *reinterpret_cast<const f32x4 *>(src + 4 * i);
 }
 
+// A row as the kernels see it.  A row whose candidates start at column s is
+// read from its 16-byte aligned base s & ~3: the `dead` = s & 3 columns in
+// front of the start are part of the view but never candidates, n counts them
+// too (dead + the visible count), and every index written is a view column
+// minus dead.  Without row starts dead is 0 and the view is the row itself.
+struct RowView {
+    const float *src;
+    int n;     // columns of the view: dead + visible
+    int dead;  // leading columns before the row's start (0..3)
+    int vis;   // visible columns from the start
+};
+
+__device__ __forceinline__ RowView row_view(const TopkArgs &a, int r, int ctx, int start) {
+    const int s = a.row_starts ? min(max(start, 0), a.width) : 0;
+    const int vis = min(max(ctx, 0), a.width - s);
+    const int base = s & ~3;
+    return RowView{a.logits + (int64_t)r * a.stride + base, vis + (s - base), s - base, vis};
+}
+
+__device__ __forceinline__ RowView row_view(const TopkArgs &a, int r) {
+    return row_view(a, r, a.ctx_lens[r], a.row_starts ? a.row_starts[r] : 0);
+}
+
+// The dead columns of group i (only group 0 has any) read as the NaN whose
+// order key is 0: below every value, never above or inside a float threshold,
+// and a non-finite value that keeps the row off the register path.
+__device__ __forceinline__ f32x4 kill_dead(f32x4 x, int i, int dead) {
+    if (dead && i == 0) {
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+            if (e < dead) x[e] = __uint_as_float(0xFFFFFFFFu);
+    }
+    return x;
+}
+
 template <class Sh>
 __device__ __forceinline__ void clear_hist(Sh &sh) {
     for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0;
@@ -153,10 +190,11 @@ struct StagedKeys {
 struct StreamKeys {
     const float *src;
     int n;
+    int dead;
     __device__ __forceinline__ uint4 group(int j) const {
         const int i = threadIdx.x + kThreads * j;
         if (4 * i >= n) return make_uint4(0u, 0u, 0u, 0u);
-        const f32x4 x = load4(src, i);
+        const f32x4 x = kill_dead(load4(src, i), i, dead);
         return make_uint4(order_key(x[0]), order_key(x[1]), order_key(x[2]), order_key(x[3]));
     }
 };
@@ -294,7 +332,7 @@ __device__ __forceinline__ int tie_column(Shared &sh, const Keys &src, int n, ui
 // groups per thread covering the row.
 template <int G, class Keys, class Bk>
 __device__ __forceinline__ void select_row(Shared &sh, const Keys &src, int n, int k, const Bk &bucket,
-                                           int32_t *out) {
+                                           int32_t *out, int dead = 0) {
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
@@ -407,7 +445,7 @@ __device__ __forceinline__ void select_row(Shared &sh, const Keys &src, int n, i
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if ((sel >> (4 * j + e)) & 1u) {
-                    if (p < k) out[p] = 4 * (t + kThreads * (c + j)) + e;
+                    if (p < k) out[p] = 4 * (t + kThreads * (c + j)) + e - dead;
                     ++p;
                 }
             }
@@ -473,7 +511,7 @@ __device__ __forceinline__ void track(float x, bool valid, uint32_t &kmax, uint3
 // registers (x[j] = group t + kThreads*j; groups at or past (n+3)/4, and
 // columns past n, hold anything): keys staged to LDS, then the selection.
 __device__ __forceinline__ void select_staged(Shared &sh, const f32x4 (&x)[kStageGroups], int n, int k,
-                                              int32_t *out) {
+                                              int32_t *out, int dead = 0) {
     const int t = threadIdx.x;
     const int n4 = (n + 3) >> 2;
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nonfinite = 0u;
@@ -507,18 +545,19 @@ __device__ __forceinline__ void select_staged(Shared &sh, const f32x4 (&x)[kStag
                 }
             }
             __syncthreads();
-            select_row<kStageGroups>(sh, sk, n, k, bucket, out);
+            select_row<kStageGroups>(sh, sk, n, k, bucket, out, dead);
         } else {
             const Bucketer<false> bucket{rr.vmax, rr.scale};
             for_each_key<kStageGroups>(sk, n, [&](int, uint32_t kx) { atomicAdd(&sh.hist[bucket(kx)], 1u); });
             __syncthreads();
-            select_row<kStageGroups>(sh, sk, n, k, bucket, out);
+            select_row<kStageGroups>(sh, sk, n, k, bucket, out, dead);
         }
     }
 }
 
 template <bool STAGE = true>
-__device__ __forceinline__ void select_full_row(Shared &sh, const float *src, int n, int k, int32_t *out) {
+__device__ __forceinline__ void select_full_row(Shared &sh, const float *src, int n, int k, int32_t *out,
+                                                int dead = 0) {
     const int t = threadIdx.x;
     const int n4 = (n + 3) >> 2;
     uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nonfinite = 0u;
@@ -528,18 +567,18 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
 #pragma unroll
         for (int j = 0; j < kStageGroups; ++j) {
             const int i = t + kThreads * j;
-            x[j] = (i < n4) ? load4(src, i) : f32x4{0.f, 0.f, 0.f, 0.f};
+            x[j] = (i < n4) ? kill_dead(load4(src, i), i, dead) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        select_staged(sh, x, n, k, out);
+        select_staged(sh, x, n, k, out, dead);
     } else {
-        const StreamKeys sk{src, n};
+        const StreamKeys sk{src, n, dead};
 #pragma unroll 1
         for (int i0 = t; i0 < n4; i0 += 4 * kThreads) {  // four float4 loads in flight
             f32x4 x[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = i0 + u * kThreads;
-                x[u] = (i < n4) ? load4(src, i) : f32x4{0.f, 0.f, 0.f, 0.f};
+                x[u] = (i < n4) ? kill_dead(load4(src, i), i, dead) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -550,7 +589,7 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
         const Bucketer<false> bucket{rr.vmax, rr.scale};
         for_each_key<kMaxGroups>(sk, n, [&](int, uint32_t kx) { atomicAdd(&sh.hist[bucket(kx)], 1u); });
         __syncthreads();
-        select_row<kMaxGroups>(sh, sk, n, k, bucket, out);
+        select_row<kMaxGroups>(sh, sk, n, k, bucket, out, dead);
     }
 }
 
@@ -784,6 +823,10 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_wave) {
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// STARTS: the call has row starts.  Rows whose start is a multiple of 4 take
+// the same path as without them, from the shifted row; any other start (its
+// view has dead columns) is set aside for the full selection.
+template <bool STARTS>
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
     __shared__ Shared sh;
     __shared__ uint32_t later[kRowsPerGroup / 32];
@@ -794,13 +837,16 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
     // read-only: through the constant address space its loads stay scalar
     const __attribute__((address_space(4))) int32_t *ctx =
         (const __attribute__((address_space(4))) int32_t *)a.ctx_lens;
-    auto visible = [&](int r) { return min(max(ctx[r], 0), a.width); };
-    auto fast_row = [&](int nn) { return k < nn && nn <= kStage; };
+    const __attribute__((address_space(4))) int32_t *starts =
+        (const __attribute__((address_space(4))) int32_t *)a.row_starts;
+    auto start_of = [&](int r) { return STARTS ? min(max(starts[r], 0), a.width) : 0; };
+    auto visible = [&](int r, int s) { return min(max(ctx[r], 0), a.width - s); };
+    auto fast_row = [&](int nn, int s) { return k < nn && nn <= kStage && (s & 3) == 0; };
     // every load at an in-row group (clamped)
-    auto prefetch = [&](int r, int nn) {
+    auto prefetch = [&](int r, int nn, int s) {
         int tt = t;
         asm volatile("" : "+v"(tt));  // addresses recomputed per row, not kept live across rows
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.logits + (int64_t)r * a.stride);
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.logits + (int64_t)r * a.stride + s);
         const int last = ((nn + 3) >> 2) - 1;
         const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
             (int)(uint32_t)(uintptr_t)(pref + (tt & ~63)));
@@ -812,16 +858,18 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
     bool any_later = false;  // uniform
     int rows_taken = 0;
     int row = blockIdx.x;
-    int n = visible(row);
-    if (fast_row(n)) prefetch(row, n);
+    int st = start_of(row);
+    int n = visible(row, st);
+    if (fast_row(n, st)) prefetch(row, n, st);
     f32x4 x[kStageGroups];
     int32_t *pend = nullptr;  // the previous row's output, its columns still in LDS
 #pragma unroll 1
     for (int m = 0;; ++m) {
         const int nxt = row + stride;
         const bool more = nxt < a.num_rows;
-        const int nn = more ? visible(nxt) : 0;
-        const bool fast = fast_row(n);
+        const int nst = more ? start_of(nxt) : 0;
+        const int nn = more ? visible(nxt, nst) : 0;
+        const bool fast = fast_row(n, st);
         if (fast) {
             wait_dma();
             __syncthreads();
@@ -835,7 +883,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
             pend = nullptr;
         }
         __syncthreads();  // pref and the kept columns have been read (the previous row is done with LDS)
-        if (more && fast_row(nn)) prefetch(nxt, nn);
+        if (more && fast_row(nn, nst)) prefetch(nxt, nn, nst);
         int32_t *out = a.idx_out + (int64_t)row * k;
         if (n <= k) {
             for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
@@ -849,6 +897,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         if (!more) break;
         row = nxt;
         n = nn;
+        st = nst;
     }
     if (pend) flush_kept(sh, k, pend);
     if (!any_later) return;
@@ -860,7 +909,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
             const int m = 32 * wd + __builtin_ctz(bits);
             bits &= bits - 1u;
             const int r = (int)blockIdx.x + m * stride;
-            select_full_row<false>(sh, a.logits + (int64_t)r * a.stride, visible(r), k, a.idx_out + (int64_t)r * k);
+            const RowView v = row_view(a, r);
+            select_full_row<false>(sh, v.src, v.n, k, a.idx_out + (int64_t)r * k, v.dead);
             __syncthreads();
         }
     }
@@ -1005,13 +1055,14 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a) {
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
-    const int n = min(max(a.ctx_lens[row], 0), a.width);
+    const RowView view = row_view(a, row);
+    const int n = view.n;
     const int k = a.k;
     const int lo = s * a.slice_len;
-    if (n <= k || lo >= n) return;
+    if (view.vis <= k || lo >= n) return;
     const int hi = min(n, lo + a.slice_len);
     const int n4 = (n + 3) >> 2;
-    const float *src = a.logits + (int64_t)row * a.stride;
+    const float *src = view.src;
 
     // the sample first (it is used first), then this thread's float4 of the slice
     const int m = n >= kSample ? kSample : n;
@@ -1024,12 +1075,15 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a) {
     } else {
         sc = 4 * ts;
     }
-    const f32x4 y = load4(src, min(sc >> 2, n4 - 1));
+    const f32x4 y = kill_dead(load4(src, min(sc >> 2, n4 - 1)), min(sc >> 2, n4 - 1), view.dead);
     if (t >= kSample / 4) sc = n;  // one sample per column: the first 512 threads
     const int c0 = lo + 4 * G * t;   // this thread's first column
     f32x4 x[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) x[j] = load4(src, min((c0 >> 2) + j, n4 - 1));
+    for (int j = 0; j < G; ++j) {
+        const int i = min((c0 >> 2) + j, n4 - 1);
+        x[j] = kill_dead(load4(src, i), i, view.dead);
+    }
 
     clear_hist(sh);
     if (t < kMBins) sh.mhist[t] = 0u;
@@ -1130,13 +1184,14 @@ __global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
-    const int n = min(max(a.ctx_lens[row], 0), a.width);
+    const RowView view = row_view(a, row);
+    const int n = view.n;
     const int k = a.k;
     int32_t *out = a.idx_out + (int64_t)row * k;
-    const float *src = a.logits + (int64_t)row * a.stride;
-    if (n <= k) {
+    const float *src = view.src;
+    if (view.vis <= k) {
         if (s == 0)
-            for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
+            for (int j = t; j < k; j += kThreads) out[j] = j < view.vis ? j : -1;
         return;
     }
     const int lo = s * a.slice_len;
@@ -1150,7 +1205,10 @@ __global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
     const int c0 = lo + 4 * G * t;
     f32x4 x[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) x[j] = load4(src, min((c0 >> 2) + j, n4 - 1));
+    for (int j = 0; j < G; ++j) {
+        const int i = min((c0 >> 2) + j, n4 - 1);
+        x[j] = kill_dead(load4(src, i), i, view.dead);
+    }
     const SplitWorkspace ws = split_ws(a);
     const int64_t rs0 = (int64_t)row * a.slices;
     const int2 mt = ws.meta[rs0 + min(l, ns - 1)];
@@ -1220,7 +1278,7 @@ __global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
     const int N = sh.split_n;
     const int cnt = sh.cross_cnt;
     if (sh.split_over || need < 1 || need > N || cnt > kCand) {
-        if (s == 0) select_full_row<false>(sh, src, n, k, out);
+        if (s == 0) select_full_row<false>(sh, src, n, k, out, view.dead);
         return;
     }
     const int bstar = sh.cross_bin;
@@ -1320,7 +1378,7 @@ __global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
     while (sel) {
         const int b = __builtin_ctz(sel);
         sel &= sel - 1u;
-        if (p < k) out[p] = c0 + b;
+        if (p < k) out[p] = c0 + b - view.dead;
         ++p;
     }
 }
@@ -1384,7 +1442,10 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEv
         // one workgroup per CU, more when a workgroup would take over kRowsPerGroup rows
         unsigned g = (unsigned)(a.num_rows < kRowsGrid ? a.num_rows : kRowsGrid);
         g = g > (unsigned)((a.num_rows + kRowsPerGroup - 1) / kRowsPerGroup) ? g : (unsigned)((a.num_rows + kRowsPerGroup - 1) / kRowsPerGroup);
-        hipExtLaunchKernelGGL(topk_rows_kernel, dim3(g), dim3(kThreads), 0, s, start, stop, 0, a);
+        if (a.row_starts)
+            hipExtLaunchKernelGGL(topk_rows_kernel<true>, dim3(g), dim3(kThreads), 0, s, start, stop, 0, a);
+        else
+            hipExtLaunchKernelGGL(topk_rows_kernel<false>, dim3(g), dim3(kThreads), 0, s, start, stop, 0, a);
     }
     return hipGetLastError();
 }

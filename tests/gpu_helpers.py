@@ -57,10 +57,10 @@ def gpu_logits(inp, dev=None, out=None, stream=None):
                           layout=dev.layout, out=out, stream=stream)
 
 
-def gpu_topk(logits_t, ctx_t, k, width=None, workspace="auto"):
+def gpu_topk(logits_t, ctx_t, k, width=None, workspace="auto", row_starts=None):
     """qsa_topk; workspace "auto" takes the split selection where the shape has
     one, None forces one workgroup per row."""
-    return qsa().topk(logits_t, ctx_t, k, width=width, workspace=workspace)
+    return qsa().topk(logits_t, ctx_t, k, width=width, workspace=workspace, row_starts=row_starts)
 
 
 TOPK_PATHS = {"split": "auto", "single": None}

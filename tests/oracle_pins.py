@@ -502,4 +502,105 @@ def pin_topk_rejects_visible_nan(lib):
     raise AssertionError("NaN inside the visible range was accepted")
 
 
+def pin_topk_row_starts_shift_invariant(lib):
+    """A row's candidates placed at column s of a wider buffer, with row start s,
+    select the same offsets as the same values at column 0 without starts
+    (sglang PR #48649 test body: per-row starts and lengths); the columns in
+    front of the start and past its end are never read (NaN there)."""
+    rng = np.random.default_rng(21)
+    W = 700
+    for kind in ("normal", "ints", "const", "relu"):
+        R = 8
+        n = rng.integers(0, 300, size=R)
+        s = rng.integers(0, W - 300, size=R)
+        s[:3] = [0, 1, 3]  # aligned and unaligned starts
+        base = qsa_inputs.make_logits(R, 300, n, seed=int(rng.integers(1000)), kind=kind)
+        wide = np.full((R, W), np.nan, dtype=np.float32)
+        for r in range(R):
+            wide[r, s[r]:s[r] + n[r]] = base[r, :n[r]]
+        for k in (1, 17, 256):
+            want = oracle.topk(base, n, k, lib=lib)
+            got = oracle.topk(wide, n, k, lib=lib, row_starts=s)
+            assert np.array_equal(got, want), (kind, k)
+            assert np.array_equal(oracle.topk(base, n, k, lib=lib, row_starts=np.zeros(R, np.int32)), want)
+
+
+def pin_topk_row_starts_bruteforce(lib):
+    """Tiny rows with starts: the unique valid selection of the window
+    [s, s + n), reported as offsets from s."""
+    rng = np.random.default_rng(22)
+    for trial in range(60):
+        W = int(rng.integers(1, 10))
+        s = int(rng.integers(0, W + 1))
+        n = int(rng.integers(0, W - s + 1))
+        k = int(rng.integers(1, 8))
+        vals = rng.choice(np.array([-2.0, -0.0, 0.0, 1.0, 1.0, 3.5, -np.inf], np.float32), size=W)
+        got = oracle.topk(vals[None, :], [n], k, lib=lib, row_starts=[s])[0]
+        win = vals[s:s + n]
+        take = min(k, n)
+        assert np.all(got[take:] == -1)
+        matches = [c for c in itertools.combinations(range(n), take) if _valid_selection(win, c, n)]
+        assert len(matches) == 1
+        assert sorted(got[:take].tolist()) == list(matches[0]), (trial, vals, s, n, k)
+
+
+def pin_topk_row_starts_clamped(lib):
+    """Starts clamp to [0, width] and lengths to what is left of the row."""
+    W = 50
+    x = np.arange(W, dtype=np.float32)[None, :].repeat(4, axis=0)
+    got = oracle.topk(x, [10, 10, 100, 5], 8, lib=lib, row_starts=[60, -7, 45, 50])
+    assert np.all(got[0] == -1)                                       # start past the width: empty
+    assert sorted(got[1].tolist()) == list(range(2, 10))              # start -7 -> 0: columns 2..9
+    assert sorted(got[2][got[2] >= 0].tolist()) == [0, 1, 2, 3, 4]    # 45 + 100 -> 5 columns left
+    assert np.count_nonzero(got[2] >= 0) == 5
+    assert np.all(got[3] == -1)                                       # start at the width: empty
+
+
+def _golden(name):
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)) as f:
+        return json.load(f)
+
+
+def pin_expand_golden(lib):
+    g = _golden("expand_example.json")
+    got = oracle.expand(np.array(g["idx"], np.int32), g["ratio"], token_lens=g["token_lens"], lib=lib)
+    assert got.tolist() == g["expected"]
+
+
+def pin_expand_properties(lib):
+    """For every slot: a token t is either -1 or lies in its column's group
+    (t // ratio == column, t % ratio == position in the group); without a token
+    bound every selected column yields its whole group; the number of tokens of
+    a column with a bound L is min(ratio, max(0, L - column * ratio)); ratio 1
+    without a bound returns the indices unchanged."""
+    rng = np.random.default_rng(23)
+    for ratio in (1, 2, 4, 7):
+        R, k = 5, 9
+        idx = np.full((R, k), -1, np.int32)
+        for r in range(R):
+            m = int(rng.integers(0, k + 1))
+            idx[r, :m] = np.sort(rng.choice(200, size=m, replace=False))
+        tl = rng.integers(0, 200 * ratio, size=R).astype(np.int32)
+        for bound in (None, tl):
+            got = oracle.expand(idx, ratio, token_lens=bound, lib=lib)
+            assert got.shape == (R, k * ratio)
+            g3 = got.reshape(R, k, ratio)
+            for r in range(R):
+                for p in range(k):
+                    c = int(idx[r, p])
+                    toks = g3[r, p]
+                    live = toks[toks >= 0]
+                    if c < 0:
+                        assert live.size == 0
+                        continue
+                    for j, t in enumerate(toks):
+                        if t >= 0:
+                            assert t // ratio == c and t % ratio == j
+                    want = ratio if bound is None else min(ratio, max(0, int(bound[r]) - c * ratio))
+                    assert live.size == want, (ratio, r, p, c)
+                    assert np.all(toks[:want] >= 0) and np.all(toks[want:] == -1)
+        if ratio == 1:
+            assert np.array_equal(oracle.expand(idx, 1, lib=lib), idx)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -178,3 +178,23 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     libs = sorted({ln.split()[-1] for ln in maps if "libamdhip64" in ln})
     assert len(libs) == 1, libs
+
+
+def test_expand_validation():
+    """qsa_expand refuses bad sizes before any launch (no HIP call)."""
+    L = m.lib
+    assert L.qsa_expand(A, -1, 8, 4, None, A, None) == m.E_INVALID
+    assert L.qsa_expand(A, 2, 0, 4, None, A, None) == m.E_INVALID
+    assert L.qsa_expand(A, 2, 8, 0, None, A, None) == m.E_INVALID
+    assert L.qsa_expand(A, 2, 1 << 22, 8, None, A, None) == m.E_RANGE
+    assert L.qsa_expand(None, 2, 8, 4, None, A, None) == m.E_INVALID
+    assert L.qsa_expand(A, 2, 8, 4, None, None, None) == m.E_INVALID
+    assert L.qsa_expand(None, 0, 8, 4, None, None, None) == m.OK  # nothing to do, nothing launched
+
+
+def test_topk_row_starts_need_no_host_check():
+    """Row starts are device data (clamped by the kernels): a pointer or NULL
+    validates the same."""
+    base = (A, 3008, A, 8, 3008, 256, A, None, 0)
+    assert m.topk_check(*base) == m.OK
+    assert m.topk_check(*base, row_starts_ptr=A) == m.OK

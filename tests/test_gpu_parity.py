@@ -819,3 +819,101 @@ def test_graph_replay_new_inputs_in_place(name):
             tk()
         torch.cuda.synchronize()
         assert torch.equal(out, ref) and torch.equal(idx, ref_idx), f"{name} replay {trial}: eager differs"
+
+
+# ---------------------------------------------------------------------------
+# row starts and expand
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", sorted(TOPK_PATHS))
+@pytest.mark.parametrize("rows,W", [(36, 30000), (9, 9000), (300, 9000)])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_topk_row_starts(rows, W, aligned, path):
+    """Per-row starts (sglang PR #48649 test body): each row's candidates are
+    the columns [s, s + n) of a shared buffer, reported as offsets from s;
+    starts that are multiples of 4 and starts that are not, starts past the
+    width, ranges cut by the width, rows that fit in k; NaN outside every
+    range.  Identical logits: exact against the oracle."""
+    k = 2048
+    rng = np.random.default_rng(rows * 31 + W + (0 if aligned else 7))
+    n = rng.integers(0, W // 2, size=rows)
+    n[: min(rows, 4)] = [W // 2, k + 1, k, 5][: min(rows, 4)]
+    s = rng.integers(0, W // 2, size=rows)
+    if aligned:
+        s &= ~3
+    else:
+        s[::2] |= 1
+    if rows > 6:
+        s[5], n[5] = W + 10, 100        # start past the width: empty
+        s[6], n[6] = W - 1000, 5000     # range cut by the width: 1000 columns
+    kinds = ["normal", "ints", "const", "relu"]
+    base = np.concatenate([qsa_inputs.make_logits(1, W, [W], seed=r + 77, kind=kinds[r % 4]) for r in range(rows)])
+    x = np.full((rows, W), np.nan, dtype=np.float32)
+    for r in range(rows):
+        st = int(min(max(s[r], 0), W))
+        m = int(min(max(n[r], 0), W - st))
+        x[r, st:st + m] = base[r, st:st + m]
+    say("topk row starts", rows, W, "aligned" if aligned else "unaligned", path)
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(n.astype(np.int32)).cuda()
+    stt = torch.from_numpy(s.astype(np.int32)).cuda()
+    oi = oracle.topk(x, n, k, row_starts=s)
+    gi = gpu_topk(xt, ct, k, workspace=TOPK_PATHS[path], row_starts=stt).cpu().numpy()
+    assert_topk_exact(gi, oi, label=f"row starts {rows}x{W}")
+    for r in range(rows):  # ascending offsets, -1 padding after them
+        v = gi[r][gi[r] >= 0]
+        assert np.all(np.diff(v) > 0) and np.all(gi[r][len(v):] == -1)
+
+
+def test_topk_row_starts_zero_equals_none():
+    """All-zero starts select exactly what no starts select, on every path."""
+    W, rows = 12000, 20
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(0, W + 1, size=rows).astype(np.int32)
+    x = qsa_inputs.make_logits(rows, W, ctx, seed=5, kind="normal")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx).cuda()
+    zero = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    say("topk zero starts")
+    for path, ws in TOPK_PATHS.items():
+        a = gpu_topk(xt, ct, 2048, workspace=ws)
+        b = gpu_topk(xt, ct, 2048, workspace=ws, row_starts=zero)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), path
+
+
+@pytest.mark.parametrize("ratio", [1, 4, 7])
+@pytest.mark.parametrize("bounded", [False, True])
+def test_expand(ratio, bounded):
+    """qsa_expand against the oracle, bit for bit: selections of various fill
+    (full, partial, empty rows), with and without a token bound."""
+    m = qsa()
+    rng = np.random.default_rng(ratio * 10 + bounded)
+    R, k = 37, 2048
+    idx = np.full((R, k), -1, np.int32)
+    for r in range(R):
+        cnt = [k, 0, 1, 100][r % 4] if r < 8 else int(rng.integers(0, k + 1))
+        idx[r, :cnt] = np.sort(rng.choice(70000, size=cnt, replace=False))
+    tl = rng.integers(0, 70000 * ratio, size=R).astype(np.int32) if bounded else None
+    say("expand", ratio, "bounded" if bounded else "no bound")
+    it = torch.from_numpy(idx).cuda()
+    tt = None if tl is None else torch.from_numpy(tl).cuda()
+    got = m.expand(it, ratio, token_lens=tt).cpu().numpy()
+    assert np.array_equal(got, oracle.expand(idx, ratio, token_lens=tl))
+
+
+def test_select_score_topk_expand_decode_verify():
+    """The full selection on the decode-verify workload: scoring, top-k and
+    expand (ratio 4, each row's token count 4 x its visible columns minus 3) as
+    three calls; the top-k is exact on the GPU's own logits, the expand bit-exact
+    on the GPU's own selection."""
+    m = qsa()
+    inp = qsa_inputs.make_config("decode_verify")
+    say("select decode_verify")
+    dev, g = run_logits(inp)
+    idx = gpu_topk(g, dev.ctx_lens, inp.topk)
+    tl = (4 * inp.ctx_lens.astype(np.int64) - 3).astype(np.int32)
+    toks = m.expand(idx, 4, token_lens=torch.from_numpy(tl).cuda()).cpu().numpy()
+    gi = idx.cpu().numpy()
+    assert_topk_exact(gi, oracle.topk(g.cpu().numpy(), inp.ctx_lens, inp.topk), label="select")
+    assert np.array_equal(toks, oracle.expand(gi, 4, token_lens=tl))

@@ -51,6 +51,14 @@ MUTATIONS = {
                       "for (int64_t j = take; j < k; ++j)\n            o[j] = 0;"),
     "topk_ctx_plus_one": ("int64_t n = ctx_lens[row];", "int64_t n = ctx_lens[row] + 1;"),
     "topk_nan_accepted": ("if (isnan(x[j]))\n                bad = 1;", ""),
+    "topk_starts_ignored": ("int64_t s = row_starts ? row_starts[row] : 0;", "int64_t s = 0;"),
+    "topk_absolute_index": ("c[j].i = (int32_t)j;", "c[j].i = (int32_t)(j + s);"),
+    "topk_start_off_by_one": ("const float *x = logits + (int64_t)row * stride + s;",
+                              "const float *x = logits + (int64_t)row * stride + (s > 0 ? s - 1 : 0);"),
+    "expand_no_bound": ("(!token_lens || tok < (int64_t)token_lens[row]);", "1;"),
+    "expand_token_offset": ("int64_t tok = (int64_t)c * ratio + j;", "int64_t tok = (int64_t)c * ratio + j + 1;"),
+    "expand_keeps_padding": ("int keep = c >= 0 &&", "int keep = c >= -1 &&"),
+    "expand_bound_inclusive": ("tok < (int64_t)token_lens[row]", "tok <= (int64_t)token_lens[row]"),
 }
 
 
