@@ -203,6 +203,23 @@ QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const in
                             const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
                             int32_t *idx_out, void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * qsa_topk_noalloc -- qsa_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same selection as qsa_topk with a workspace of
+ * qsa_topk_workspace_bytes(num_rows, width, k) bytes, but the workspace is a
+ * fixed 9 MiB device array held by the library (one per GPU, until the process
+ * ends), so the call allocates nothing.  Every supported shape fits (the
+ * largest needs 8,652,800 bytes); a shape that would not returns QSA_E_RANGE.
+ * The array is that of the calling thread's current device, which must be the
+ * device of `stream`.  Calls on one GPU share the array: calls that overlap
+ * (concurrent streams, several threads) race; order them on one stream.
+ * Arguments and other errors as qsa_topk.
+ */
+QSA_API qsa_status qsa_topk_noalloc(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                                    const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
+                                    int32_t *idx_out, void *stream);
+
 /* Bytes of workspace qsa_topk uses for this shape; 0 when every row is selected
  * by one workgroup whatever the workspace.  Host-only, no HIP call; k does not
  * change the size in this version of the library. */

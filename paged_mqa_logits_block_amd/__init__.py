@@ -25,8 +25,8 @@ BF16, FP8_E4M3FN, FP16 = 0, 1, 2
 KV_PAGED, KV_COPACKED, KV_COPACKED_SHUFFLED = 0, 1, 2
 
 EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
-            "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_expand",
-            "qsa_last_error", "qsa_version")
+            "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_topk_noalloc",
+            "qsa_expand", "qsa_last_error", "qsa_version")
 
 
 class QsaError(RuntimeError):
@@ -71,6 +71,8 @@ def _load():
     lib.qsa_topk_timed.restype = ctypes.c_int
     lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp, i64]
     lib.qsa_topk_check.restype = ctypes.c_int
+    lib.qsa_topk_noalloc.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp]
+    lib.qsa_topk_noalloc.restype = ctypes.c_int
     lib.qsa_expand.argtypes = [i32p, i32, i32, i32, i32p, i32p, vp]
     lib.qsa_expand.restype = ctypes.c_int
     lib.qsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
@@ -250,6 +252,30 @@ def topk(logits, ctx_lens, k: int, *, width: Optional[int] = None, row_starts=No
     else:
         st = lib.qsa_topk_timed(*args, _event(events[0]), _event(events[1]))
     _raise_on(st)
+    return out
+
+
+def topk_noalloc(logits, ctx_lens, k: int, *, width: Optional[int] = None, row_starts=None, out=None,
+                 stream=None):
+    """``qsa_topk_noalloc``: as ``topk`` with the library-held scratch instead of
+    a workspace (the call allocates no device memory; ``out`` may be given so
+    that nothing is allocated here either)."""
+    import torch
+    _require(logits.is_cuda and ctx_lens.is_cuda, "logits and ctx_lens must be device tensors")
+    _require(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
+             "logits must be f32 [R, >=width] with unit column stride")
+    _require(ctx_lens.dtype == torch.int32 and ctx_lens.is_contiguous(), "ctx_lens must be contiguous int32")
+    R = int(logits.shape[0])
+    if row_starts is not None:
+        _check_rows_i32("row_starts", row_starts, R)
+    width = int(logits.shape[1]) if width is None else int(width)
+    if out is None:
+        out = torch.empty((R, k), dtype=torch.int32, device=logits.device)
+    _require(out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (R, k),
+             "out must be contiguous int32 [R, k]")
+    stride = int(logits.stride(0)) if R > 0 else width
+    _raise_on(lib.qsa_topk_noalloc(_ptr(logits), stride, _ptr(ctx_lens), _ptr(row_starts), R, width, int(k),
+                                   _ptr(out), _stream(stream)))
     return out
 
 

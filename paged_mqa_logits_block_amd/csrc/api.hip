@@ -230,6 +230,25 @@ qsa_status qsa_topk_timed(const float *logits, int64_t logits_stride, const int3
     return ok();
 }
 
+qsa_status qsa_topk_noalloc(const float *logits, int64_t logits_stride, const int32_t *ctx_lens,
+                            const int32_t *row_starts, int32_t num_rows, int32_t width, int32_t k,
+                            int32_t *idx_out, void *stream) {
+    qsa_status st = check_topk(logits, logits_stride, ctx_lens, num_rows, width, k, idx_out, nullptr, 0);
+    if (st != QSA_OK) return st;
+    if (num_rows == 0) return ok();
+    const int64_t need = qsa::topk_workspace_bytes(num_rows, width);
+    if (need > qsa::kTopkScratchBytes)
+        return fail(QSA_E_RANGE, "the selection needs %lld bytes of scratch; the library holds %lld",
+                    (long long)need, (long long)qsa::kTopkScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        hipError_t e = qsa::topk_scratch(&ws);
+        if (e != hipSuccess) return fail(QSA_E_HIP, "scratch lookup failed: %s", hipGetErrorString(e));
+    }
+    return qsa_topk_timed(logits, logits_stride, ctx_lens, row_starts, num_rows, width, k, idx_out, ws, need,
+                          stream, nullptr, nullptr);
+}
+
 qsa_status qsa_expand(const int32_t *idx, int32_t num_rows, int32_t k, int32_t ratio, const int32_t *token_lens,
                       int32_t *tokens_out, void *stream) {
     if (num_rows < 0) return fail(QSA_E_INVALID, "num_rows = %d < 0", num_rows);

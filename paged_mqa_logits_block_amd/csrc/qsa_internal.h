@@ -97,6 +97,13 @@ struct TopkPlan {
 int topk_groups_for_width(int width);  // 1 if the width is supported, else 0
 TopkPlan plan_topk(int num_rows, int width);
 int64_t topk_workspace_bytes(int num_rows, int width);  // 0: no workspace used
+// Bytes of the library-held split-selection scratch per GPU: the largest
+// workspace any supported shape uses (8,652,800 bytes, at 128 rows x 49,169
+// columns), rounded up to 9 MiB.
+constexpr int64_t kTopkScratchBytes = (int64_t)9 << 20;
+// Device address of that scratch on the calling thread's current device
+// (looked up on the first call per device).
+hipError_t topk_scratch(void **ptr);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 
 // Selected compressed columns -> tokens (qsa_expand).

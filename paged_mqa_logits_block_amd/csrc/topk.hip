@@ -37,6 +37,8 @@
 //     group, the kept count is packed three groups to a word; DPP wave scans of
 //     the packed words give every lane its offset inside the wave, and one scan
 //     of per-(group, wave) totals gives each wave's offset.
+#include <mutex>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -1415,6 +1417,40 @@ int64_t topk_workspace_bytes(int num_rows, int width) {
     if (p.slices < 2) return 0;
     const int64_t rs = (int64_t)num_rows * p.slices;
     return split_meta_bytes(num_rows, p.slices) + rs * kMBins * 4 + (rs << p.cand_shift) * 8;
+}
+
+// ---- library-held scratch for callers that cannot allocate ------------------
+//
+// The split selection's workspace, as a fixed device array of the library: one
+// copy per GPU, at its own address, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a handle);
+// it passes the device address hipGetSymbolAddress gives for the current
+// device, looked up once per device.  The split workspace needs no
+// initialisation (every count, histogram and used member slot is written by
+// the window kernel before the resolve kernel reads it), so nothing is
+// cleared.  Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kTopkScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t topk_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 template <int G>
