@@ -204,6 +204,52 @@ QSA_API qsa_status qsa_topk(const float *logits, int64_t logits_stride, const in
                             int32_t *idx_out, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * qsa_paged_logits_topk -- qsa_paged_logits, then qsa_topk on the logits it wrote
+ * (row stride shape->out_stride, candidates [0, clamp(ctx_lens[r], 0, width)),
+ * no row starts), in one call: the logits in `out` and the indices in idx_out
+ * are exactly those of the two calls.  The pages time the whole selection, not
+ * the scoring alone (vLLM PR #62589, "Performance": score + top-k, CUDA events
+ * around both); here, for shapes that the per-tile scorer takes with 4 or fewer
+ * heads (decode batches), its epilogue also writes each row's 16 largest scores
+ * of every 64-column chunk into the workspace, and one selection kernel works
+ * from those lists (a quarter of the row) instead of a sampling kernel and a
+ * resolve kernel over the whole row.  Other shapes run the scoring kernel and
+ * the plain selection.
+ *
+ *   q .. shape   as qsa_paged_logits (out is both its output and the
+ *                selection's input).
+ *   k, idx_out   as qsa_topk ([num_rows][k] int32, ascending, -1 padded).
+ *   workspace    device scratch owned by the caller of at least
+ *                qsa_paged_logits_topk_workspace_bytes(shape, k) bytes, 16-byte
+ *                aligned (else QSA_E_INVALID / QSA_E_ALIGN), or NULL: no fusion
+ *                and one workgroup per row for the selection (the results do
+ *                not change).  No initialisation needed, nothing kept between
+ *                calls; calls sharing a workspace must be ordered.
+ *
+ * Errors: those of qsa_paged_logits and of qsa_topk.  Device preconditions: both
+ * calls'.  Asynchronous on `stream`; graph-capturable.
+ */
+QSA_API qsa_status qsa_paged_logits_topk(const void *q, const float *w, const void *kcache, const float *kscale,
+                                         const int32_t *block_table, const int32_t *ctx_lens,
+                                         const int32_t *row_to_req, float *out, const qsa_logits_shape *shape,
+                                         int32_t k, int32_t *idx_out, void *workspace, int64_t workspace_bytes,
+                                         void *stream);
+
+/* Bytes of workspace qsa_paged_logits_topk uses for this shape (0 when none);
+ * host-only, no HIP call. */
+QSA_API int64_t qsa_paged_logits_topk_workspace_bytes(const qsa_logits_shape *shape, int32_t k);
+
+/* qsa_paged_logits_topk with dispatch-recorded events (as qsa_paged_logits_timed):
+ * start_event at the scoring kernel's start, mid_event at its end, stop_event at
+ * the end of the selection.  Events may be NULL. */
+QSA_API qsa_status qsa_paged_logits_topk_timed(const void *q, const float *w, const void *kcache,
+                                               const float *kscale, const int32_t *block_table,
+                                               const int32_t *ctx_lens, const int32_t *row_to_req, float *out,
+                                               const qsa_logits_shape *shape, int32_t k, int32_t *idx_out,
+                                               void *workspace, int64_t workspace_bytes, void *stream,
+                                               void *start_event, void *mid_event, void *stop_event);
+
+/*
  * qsa_topk_noalloc -- qsa_topk for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same selection as qsa_topk with a workspace of

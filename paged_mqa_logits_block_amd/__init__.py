@@ -26,6 +26,7 @@ KV_PAGED, KV_COPACKED, KV_COPACKED_SHUFFLED = 0, 1, 2
 
 EXPORTED = ("qsa_paged_logits", "qsa_paged_logits_timed", "qsa_paged_logits_check", "qsa_topk",
             "qsa_topk_timed", "qsa_topk_check", "qsa_topk_workspace_bytes", "qsa_topk_noalloc",
+            "qsa_paged_logits_topk", "qsa_paged_logits_topk_timed", "qsa_paged_logits_topk_workspace_bytes",
             "qsa_expand", "qsa_last_error", "qsa_version")
 
 
@@ -71,6 +72,13 @@ def _load():
     lib.qsa_topk_timed.restype = ctypes.c_int
     lib.qsa_topk_check.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp, i64]
     lib.qsa_topk_check.restype = ctypes.c_int
+    lib.qsa_paged_logits_topk.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp, i32, i32p, vp, i64, vp]
+    lib.qsa_paged_logits_topk.restype = ctypes.c_int
+    lib.qsa_paged_logits_topk_timed.argtypes = [vp, vp, vp, vp, i32p, i32p, i32p, vp, sp, i32, i32p, vp, i64, vp,
+                                                vp, vp, vp]
+    lib.qsa_paged_logits_topk_timed.restype = ctypes.c_int
+    lib.qsa_paged_logits_topk_workspace_bytes.argtypes = [sp, i32]
+    lib.qsa_paged_logits_topk_workspace_bytes.restype = ctypes.c_int64
     lib.qsa_topk_noalloc.argtypes = [vp, i64, i32p, i32p, i32, i32, i32, i32p, vp]
     lib.qsa_topk_noalloc.restype = ctypes.c_int
     lib.qsa_expand.argtypes = [i32p, i32, i32, i32, i32p, i32p, vp]
@@ -368,3 +376,69 @@ class PreparedTopk:
         if st != OK:
             _raise_on(st)
         return self.out
+
+
+def paged_logits_topk_workspace_bytes(shape: LogitsShape, k: int) -> int:
+    """``qsa_paged_logits_topk_workspace_bytes`` for a shape (see ``make_shape``)."""
+    return int(lib.qsa_paged_logits_topk_workspace_bytes(ctypes.byref(shape), int(k)))
+
+
+class PreparedLogitsTopk:
+    """A validated ``qsa_paged_logits_topk`` call on fixed tensors: scoring into
+    ``out`` and the top-k of those logits into ``idx``, fused where the shape
+    allows; ``workspace`` "auto" allocates it once here (None: no fusion)."""
+
+    def __init__(self, q, kcache, block_table, ctx_lens, row_to_req, out, idx, *, k: int, width: int,
+                 block_size: int, w=None, kscale=None, layout: int = KV_PAGED, workspace="auto", stream=None):
+        import torch
+        R = int(q.shape[0])
+        _require(out.dtype == torch.float32 and out.dim() == 2 and out.stride(1) == 1,
+                 "out must be f32 [R, >=width]")
+        _require(idx.dtype == torch.int32 and idx.is_contiguous() and tuple(idx.shape) == (R, k),
+                 "idx must be contiguous int32 [R, k]")
+        self.shape = make_shape(q, kcache, block_table, width=width, block_size=block_size,
+                                layout=layout, out_stride=out.stride(0) if R > 0 else width)
+        ws = None
+        if isinstance(workspace, str):
+            _require(workspace == "auto", 'workspace must be "auto", None or a device tensor')
+            nbytes = paged_logits_topk_workspace_bytes(self.shape, k)
+            if nbytes > 0:
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        elif workspace is not None:
+            ws = workspace
+        self.workspace = ws
+        self._keep = (q, kcache, block_table, ctx_lens, row_to_req, out, idx, w, kscale, ws)
+        self._args = (_ptr(q), _ptr(w), _ptr(kcache), _ptr(kscale), _ptr(block_table), _ptr(ctx_lens),
+                      _ptr(row_to_req), _ptr(out), ctypes.byref(self.shape), int(k), _ptr(idx), _ptr(ws),
+                      0 if ws is None else int(ws.numel()), _stream(stream))
+        _raise_on(lib.qsa_paged_logits_check(*self._args[:9]))
+        self.out, self.idx = out, idx
+
+    def __call__(self, events=None):
+        if events is None:
+            st = lib.qsa_paged_logits_topk(*self._args)
+        else:
+            st = lib.qsa_paged_logits_topk_timed(*self._args, *(_event(e) for e in events))
+        if st != OK:
+            _raise_on(st)
+        return self.out, self.idx
+
+
+def paged_logits_topk(q, kcache, block_table, ctx_lens, row_to_req, *, k: int, width: int, block_size: int,
+                      w=None, kscale=None, layout: int = KV_PAGED, out=None, idx=None, workspace="auto",
+                      stream=None):
+    """``qsa_paged_logits_topk``: (logits [R, width], indices [R, k]), exactly as
+    ``paged_logits`` followed by ``topk`` on its result, fused where the shape
+    allows."""
+    import torch
+    R = int(q.shape[0])
+    if out is None:
+        out = torch.empty((R, (width + 3) & ~3), dtype=torch.float32, device=q.device)[:, :width]
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=q.device)
+    call = PreparedLogitsTopk(q, kcache, block_table, ctx_lens, row_to_req, out, idx, k=k, width=width,
+                              block_size=block_size, w=w, kscale=kscale, layout=layout, workspace=workspace,
+                              stream=stream)
+    if call.workspace is not None:
+        call.workspace.record_stream(_torch_stream(stream))
+    return call()

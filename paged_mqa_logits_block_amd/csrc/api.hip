@@ -107,6 +107,22 @@ qsa_status check_topk(const float *logits, int64_t stride, const int32_t *ctx_le
     return ok();
 }
 
+// The fused call writes chunk candidates from the scoring epilogue when the
+// per-tile kernel scores the shape with 4 or fewer heads (one score per lane
+// and 16-column tile, 64-column chunks); every other shape runs the scoring
+// kernel and then the plain selection.
+bool fused_candidates(const qsa::LogitsPlan &p, const qsa_logits_shape *s) {
+    return !p.prefill && !p.mtp && p.iters == 0 && s->num_heads <= 4 && p.tiles_per_prog == 4;
+}
+
+int64_t fused_workspace_bytes(const qsa_logits_shape *s) {
+    if (s->num_rows <= 0 || s->width <= 0) return 0;
+    const qsa::LogitsPlan p = qsa::plan_logits(s->k_dtype, s->kv_layout, s->head_dim, s->num_heads, s->num_rows,
+                                               s->num_reqs, s->width, s->block_size, s->out_stride);
+    if (fused_candidates(p, s)) return (int64_t)s->num_rows * ((s->width + 63) / 64) * 128;
+    return qsa::topk_workspace_bytes(s->num_rows, s->width);
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,19 +140,16 @@ qsa_status qsa_paged_logits(const void *q, const float *w, const void *kcache, c
                                   nullptr, nullptr);
 }
 
-qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kcache, const float *kscale,
-                                  const int32_t *block_table, const int32_t *ctx_lens,
-                                  const int32_t *row_to_req, float *out, const qsa_logits_shape *s,
-                                  void *stream, void *start_event, void *stop_event) {
-    qsa_status st = check_logits(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s);
-    if (st != QSA_OK) return st;
-    if (s->num_rows == 0 || s->width == 0) return ok();
+}  // extern "C"
+
+namespace {
+
+// The launch description of a checked qsa_paged_logits call.
+qsa::LogitsArgs logits_args(const void *q, const float *w, const void *kcache, const float *kscale,
+                            const int32_t *block_table, const int32_t *ctx_lens, const int32_t *row_to_req,
+                            float *out, const qsa_logits_shape *s, const qsa::LogitsPlan &plan) {
     const bool fp8 = s->k_dtype == QSA_FP8_E4M3FN;
     const int64_t elt = fp8 ? 1 : 2;
-    // the kernels' dtype codes are the qsa_dtype values
-    static_assert(QSA_BF16 == qsa::kBF16 && QSA_FP8_E4M3FN == qsa::kFP8 && QSA_FP16 == qsa::kFP16, "dtype codes");
-    qsa::LogitsPlan plan = qsa::plan_logits(s->k_dtype, s->kv_layout, s->head_dim, s->num_heads, s->num_rows, s->num_reqs, s->width, s->block_size,
-                                                s->out_stride);
     qsa::LogitsArgs a = {};
     a.q = q;
     a.w = w;
@@ -157,8 +170,6 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     a.num_row_tiles = (s->num_rows + plan.rows_per_tile - 1) / plan.rows_per_tile;
     const int chunk_cols = 16 * plan.tiles_per_prog;
     a.num_chunks = (s->width + chunk_cols - 1) / chunk_cols;
-    if ((int64_t)a.num_row_tiles * a.num_chunks > 0x7FFFFFFF)
-        return fail(QSA_E_RANGE, "grid too large (%d row tiles x %d chunks)", a.num_row_tiles, a.num_chunks);
     a.dtype = s->k_dtype;
     a.layout = s->kv_layout;
     a.num_blocks = s->num_blocks;
@@ -168,11 +179,113 @@ qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kca
     a.block_bytes = (int64_t)s->block_size * a.key_stride + (s->kv_layout != QSA_KV_PAGED ? 4 * s->block_size : 0);
     a.scale_offset = (int64_t)s->block_size * a.key_stride;
     a.iters = plan.iters;
+    a.cand = nullptr;
+    return a;
+}
+
+qsa::LogitsPlan plan_of(const qsa_logits_shape *s) {
+    // the kernels' dtype codes are the qsa_dtype values
+    static_assert(QSA_BF16 == qsa::kBF16 && QSA_FP8_E4M3FN == qsa::kFP8 && QSA_FP16 == qsa::kFP16, "dtype codes");
+    return qsa::plan_logits(s->k_dtype, s->kv_layout, s->head_dim, s->num_heads, s->num_rows, s->num_reqs, s->width,
+                            s->block_size, s->out_stride);
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_paged_logits_timed(const void *q, const float *w, const void *kcache, const float *kscale,
+                                  const int32_t *block_table, const int32_t *ctx_lens,
+                                  const int32_t *row_to_req, float *out, const qsa_logits_shape *s,
+                                  void *stream, void *start_event, void *stop_event) {
+    qsa_status st = check_logits(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s);
+    if (st != QSA_OK) return st;
+    if (s->num_rows == 0 || s->width == 0) return ok();
+    const qsa::LogitsPlan plan = plan_of(s);
+    qsa::LogitsArgs a = logits_args(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s, plan);
+    if ((int64_t)a.num_row_tiles * a.num_chunks > 0x7FFFFFFF)
+        return fail(QSA_E_RANGE, "grid too large (%d row tiles x %d chunks)", a.num_row_tiles, a.num_chunks);
     hipError_t e = qsa::launch_paged_logits(a, plan, static_cast<hipStream_t>(stream),
                                             static_cast<hipEvent_t>(start_event),
                                             static_cast<hipEvent_t>(stop_event));
     if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+int64_t qsa_paged_logits_topk_workspace_bytes(const qsa_logits_shape *shape, int32_t k) {
+    (void)k;
+    if (!shape) return 0;
+    return fused_workspace_bytes(shape);
+}
+
+qsa_status qsa_paged_logits_topk_timed(const void *q, const float *w, const void *kcache, const float *kscale,
+                                       const int32_t *block_table, const int32_t *ctx_lens,
+                                       const int32_t *row_to_req, float *out, const qsa_logits_shape *s,
+                                       int32_t k, int32_t *idx_out, void *workspace, int64_t workspace_bytes,
+                                       void *stream, void *start_event, void *mid_event, void *stop_event) {
+    qsa_status st = check_logits(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s);
+    if (st != QSA_OK) return st;
+    st = check_topk(out, s->out_stride, ctx_lens, s->num_rows, s->width, k, idx_out, nullptr, 0);
+    if (st != QSA_OK) return st;
+    const int64_t need = fused_workspace_bytes(s);
+    if (workspace) {
+        if (workspace_bytes < need)
+            return fail(QSA_E_INVALID, "workspace_bytes = %lld < %lld", (long long)workspace_bytes, (long long)need);
+        if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+            return fail(QSA_E_ALIGN, "workspace must be 16-byte aligned");
+    }
+    if (s->num_rows == 0) return ok();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const qsa::LogitsPlan plan = plan_of(s);
+    qsa::LogitsArgs a = logits_args(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, s, plan);
+    if ((int64_t)a.num_row_tiles * a.num_chunks > 0x7FFFFFFF)
+        return fail(QSA_E_RANGE, "grid too large (%d row tiles x %d chunks)", a.num_row_tiles, a.num_chunks);
+    const bool fused = workspace && s->width > 0 && fused_candidates(plan, s);
+    if (fused) a.cand = static_cast<uint32_t *>(workspace);
+    hipError_t e = hipSuccess;
+    if (s->width > 0)
+        e = qsa::launch_paged_logits(a, plan, hs, static_cast<hipEvent_t>(start_event),
+                                     static_cast<hipEvent_t>(mid_event));
+    if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    qsa::TopkArgs t = {};
+    t.logits = out;
+    t.stride = s->out_stride;
+    t.ctx_lens = ctx_lens;
+    t.row_starts = nullptr;
+    t.num_rows = s->num_rows;
+    t.width = s->width;
+    t.k = k;
+    t.idx_out = idx_out;
+    t.slices = 1;
+    t.slice_len = s->width;
+    if (fused) {
+        t.cand = a.cand;
+        t.cand_chunks = a.num_chunks;
+        t.cap = a.cap;
+        e = qsa::launch_topk_cand(t, hs, nullptr, static_cast<hipEvent_t>(stop_event));
+    } else {
+        if (workspace) {
+            const qsa::TopkPlan p = qsa::plan_topk(s->num_rows, s->width);
+            if (p.slices > 1) {
+                t.workspace = static_cast<uint8_t *>(workspace);
+                t.slices = p.slices;
+                t.slice_len = p.slice_len;
+                t.groups = p.groups;
+                t.cand_shift = p.cand_shift;
+            }
+        }
+        e = qsa::launch_topk(t, hs, nullptr, static_cast<hipEvent_t>(stop_event));
+    }
+    if (e != hipSuccess) return fail(QSA_E_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+qsa_status qsa_paged_logits_topk(const void *q, const float *w, const void *kcache, const float *kscale,
+                                 const int32_t *block_table, const int32_t *ctx_lens, const int32_t *row_to_req,
+                                 float *out, const qsa_logits_shape *shape, int32_t k, int32_t *idx_out,
+                                 void *workspace, int64_t workspace_bytes, void *stream) {
+    return qsa_paged_logits_topk_timed(q, w, kcache, kscale, block_table, ctx_lens, row_to_req, out, shape, k,
+                                       idx_out, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 int64_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t width, int32_t k) {

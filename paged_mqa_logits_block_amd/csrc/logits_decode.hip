@@ -30,6 +30,70 @@
 namespace qsa {
 namespace {
 
+// ---- the selection's first pass, in the epilogue -------------------------
+//
+// With CAND the kernel also writes, for every stored row and 64-column chunk,
+// the chunk's 32 largest scores as packed keys: the top 26 bits of the score's
+// order key (a float order with -0 = +0) over 63 - (column in the chunk).  The
+// packed order is (truncated score desc, column asc), every key of a row is
+// distinct, and the resolve step of the selection works on these lists (half
+// the row) instead of the row.  Columns that are not candidates (past the
+// row's visible count) get key 0, below every packed key.
+
+__device__ __forceinline__ void cas_desc(uint32_t &a, uint32_t &b) {
+    const uint32_t hi = max(a, b), lo = min(a, b);
+    a = hi;
+    b = lo;
+}
+
+// k[s] against the partner lane's k[REV ? 3 - s : s]; upper lanes keep the
+// larger of each pair, the others the smaller
+template <int CTRL, bool REV>
+__device__ __forceinline__ void half_clean(uint32_t (&k)[4], bool upper) {
+    uint32_t p[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) p[s] = dpp_u32<CTRL>(k[REV ? 3 - s : s]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k[s] = upper ? max(k[s], p[s]) : min(k[s], p[s]);
+}
+
+// a bitonic run of 4 in one lane, sorted descending
+__device__ __forceinline__ void sort_bitonic4(uint32_t (&k)[4]) {
+    cas_desc(k[0], k[2]);
+    cas_desc(k[1], k[3]);
+    cas_desc(k[0], k[1]);
+    cas_desc(k[2], k[3]);
+}
+
+// The 32 largest of the 64 keys a 16-lane row holds, 4 per lane (every lane
+// of the wave runs it; each row works on its own keys), by bitonic merging:
+// each lane sorts its 4; lane pairs merge into sorted runs of 8, lane quads
+// into sorted runs of 16 and 8-lane halves into sorted runs of 32; lanes 0..7
+// keep the larger 32 of the two halves' (against lanes 15..8).  On return lanes
+// 0..7 of every row hold its 32 largest keys, in no particular order.
+// i = lane & 15.
+__device__ __forceinline__ void top32_of_64(uint32_t (&k)[4], int i) {
+    cas_desc(k[0], k[1]);
+    cas_desc(k[2], k[3]);
+    cas_desc(k[0], k[2]);
+    cas_desc(k[1], k[3]);
+    cas_desc(k[1], k[2]);
+    half_clean<kDppXor1, true>(k, (i & 1) == 0);
+    sort_bitonic4(k);
+    half_clean<kDppXor3, true>(k, (i & 2) == 0);
+    half_clean<kDppXor1, false>(k, (i & 1) == 0);
+    sort_bitonic4(k);
+    half_clean<kDppHalfMirror, true>(k, (i & 4) == 0);
+    half_clean<kDppXor2, false>(k, (i & 2) == 0);
+    half_clean<kDppXor1, false>(k, (i & 1) == 0);
+    sort_bitonic4(k);
+    uint32_t p[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) p[s] = dpp_u32<kDppMirror>(k[3 - s]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k[s] = max(k[s], p[s]);
+}
+
 // H heads, MT stacked 16-row tiles, TPW 16-column tiles per program.
 // GATHER: the block size is not a multiple of 16 (down to one key per block),
 // so a 16-column tile may straddle blocks: every lane reads the table entry of
@@ -37,7 +101,8 @@ namespace {
 // its key slice from that block.
 // D: head dim, 128 or 64 (a template argument, so that D = 128 carries no
 // run-time test in the hot loop).
-template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE, bool GATHER, int D>
+// CAND: also write the chunk candidates of the selection (4 or fewer heads, 64-column chunks).
+template <int DT, int H, int MT, int TPW, bool HAS_W, bool HAS_SCALE, bool GATHER, int D, bool CAND>
 __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     typedef Frag<DT> F;
     constexpr int M = 16 * MT;
@@ -60,6 +125,7 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
     // quad transpose to 16-byte stores whose adjacent lanes write different
     // 64-byte segments (about 25 us).
     constexpr bool LDS_STORE = H >= 8;
+    static_assert(!CAND || (H <= 4 && TPW == 4), "candidates: one score per lane and tile, 64-column chunks");
     constexpr int CW = TPW * 16;        // columns per program
     constexpr int PER = RT * CW / 64;   // floats per lane after the transpose
     constexpr int VEC = PER >= 4 ? 4 : PER;
@@ -381,24 +447,53 @@ __global__ __launch_bounds__(64) void paged_logits_kernel(LogitsArgs a) {
                     }
                 }
             }
+            if constexpr (CAND) {
+                // the chunk's 32 largest stored scores of each row, as packed keys
+                const int i = l & 15;
+#pragma unroll
+                for (int j = 0; j < NR; ++j) {
+                    uint32_t key[4];
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        const int cc = 16 * t + i;
+                        // a candidate column is visible, hence live: the stored value
+                        const float v = ok[t] ? val[t][j] * kscale[t] : qnan;
+                        key[t] = c0 + cc < st_ctx[j] ? ((order_key(v) & ~63u) | (uint32_t)(63 - cc)) : 0u;
+                    }
+                    top32_of_64(key, i);
+                    if (i < 8 && ((set >> st_rr[j]) & 1u) && c0 < st_ctx[j]) {
+                        uint32_t *dst = a.cand + ((int64_t)(row0 + st_rr[j]) * a.num_chunks + chunk) * 32 + 4 * i;
+                        *reinterpret_cast<uint4 *>(dst) = make_uint4(key[0], key[1], key[2], key[3]);
+                    }
+                }
+            }
         }
     }
 }
 
-template <int DT, int H, int MT, int TPW, bool GATHER, int D>
-hipError_t launch_hg(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int DT, int H, int MT, int TPW, bool GATHER, int D, bool CAND>
+hipError_t launch_hgc(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     dim3 grid((unsigned)a.num_row_tiles * (unsigned)a.num_chunks), block(64);
     const bool has_w = a.w != nullptr;
     const bool has_s = DT == kFP8 && (a.layout != 0 || a.kscale != nullptr);
     if (has_w && has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, true, GATHER, D, CAND>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_w)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, true, false, GATHER, D, CAND>), grid, block, 0, s, e0, e1, 0, a);
     else if (has_s)
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, true, GATHER, D, CAND>), grid, block, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false, GATHER, D>), grid, block, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((paged_logits_kernel<DT, H, MT, TPW, false, false, GATHER, D, CAND>), grid, block, 0, s, e0, e1, 0, a);
     return hipGetLastError();
+}
+
+template <int DT, int H, int MT, int TPW, bool GATHER, int D>
+hipError_t launch_hg(const LogitsArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if constexpr (H <= 4 && TPW == 4) {
+        if (a.cand) return launch_hgc<DT, H, MT, TPW, GATHER, D, true>(a, s, e0, e1);
+    }
+    if (a.cand) return hipErrorInvalidValue;  // the planner never asks for this
+    return launch_hgc<DT, H, MT, TPW, GATHER, D, false>(a, s, e0, e1);
 }
 
 template <int DT, int H, int MT, int TPW>

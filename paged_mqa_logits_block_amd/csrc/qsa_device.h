@@ -149,6 +149,17 @@ __device__ __forceinline__ float relu(float x) {
     return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e+38f);
 }
 
+// DPP lane patterns inside each 16-lane row: quad_perm [1,0,3,2] (lane ^ 1),
+// [2,3,0,1] (lane ^ 2), [3,2,1,0] (lane ^ 3), row_half_mirror (lane ^ 7) and
+// row_mirror (lane ^ 15)
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppXor3 = 0x1B, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// value of `v` in the lane given by the DPP pattern (all lanes active)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 // f32 bits -> u32 whose unsigned order is the float order; -0 is folded onto +0
 // so that the two zeros compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -39,6 +39,8 @@ struct LogitsArgs {
     int64_t scale_offset;   // co-packed: byte offset of the scales inside a block
     int32_t iters;          // looped variant: key-tile groups per program
     int32_t pad2_;
+    uint32_t *cand;         // or null: the per-tile kernel also writes each row's chunk candidates
+                            // ([rows][num_chunks][32] packed keys) for the fused selection
 };
 
 // Variant chosen for a call: rows per tile and column tiles per program.
@@ -83,6 +85,11 @@ struct TopkArgs {
     int32_t slice_len;   // columns per slice, a multiple of 4
     int32_t groups;      // consecutive float4 per thread covering a slice
     int32_t cand_shift;  // log2 of the member slots per slice
+    // fused selection: the scoring kernel's chunk candidates ([rows][cand_chunks][32]
+    // packed keys) and the visible limit of that scoring (min(width, table columns))
+    const uint32_t *cand;
+    int32_t cand_chunks;
+    int32_t cap;
 };
 
 // How a top-k call is spread: one workgroup per row, or `slices` workgroups
@@ -105,6 +112,8 @@ constexpr int64_t kTopkScratchBytes = (int64_t)9 << 20;
 // (looked up on the first call per device).
 hipError_t topk_scratch(void **ptr);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
+// The fused selection's resolve: one workgroup per row, from a.cand.
+hipError_t launch_topk_cand(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 
 // Selected compressed columns -> tokens (qsa_expand).
 struct ExpandArgs {

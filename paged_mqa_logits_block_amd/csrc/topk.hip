@@ -1385,6 +1385,297 @@ __global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
     }
 }
 
+// ---- fused selection: the resolve from the scoring kernel's candidates -----
+//
+// The per-tile scoring kernel has written, for every row and 64-column chunk,
+// the chunk's 32 largest scores as packed keys (the score's order key with its
+// low 6 bits replaced by 63 - the column in the chunk: the order (truncated
+// score desc, column asc), distinct within a row).  One workgroup per row,
+// thread t holding the list of chunk t (and t + 1024) in registers:
+//
+//  1. the lists' range and count (a list covers every column of a chunk with
+//     at most 32 visible ones);
+//  2. a bucket histogram over the truncated scores, the crossing bucket, and
+//     among its members the k-th largest packed key P;
+//  3. keys whose truncated score is above P's are kept; those equal to it (P,
+//     and rarely columns within 64 ulp of it) are ranked on their exact logits
+//     (value desc, column asc) for the remaining places.  A full chunk whose
+//     32nd key has P's truncated score or more might hold unlisted columns of
+//     the selection: then, as for a non-finite candidate, fewer listed keys than
+//     k, a crowded bucket or tie group, or a row whose visible count exceeds
+//     what the scoring wrote candidates for, the row takes the full selection
+//     from its logits, so the result is always the unique one;
+//  4. the kept columns, marked in a bitmask of the row, are written in order.
+constexpr int kCandChunk = 64;                 // columns per candidate list
+constexpr int kCandList = 32;                  // keys per list
+constexpr int kCandTies = 64;                  // tie group ranked by one wave
+static_assert(kMaxWidth % kCandChunk == 0, "whole chunks");
+static_assert(kMaxWidth / 32 <= kStage, "the bitmask fits the staging area");
+
+// KPT keys per thread: thread t holds keys [KPT t, KPT t + KPT) of the row's
+// concatenated lists (16: half a list, while the row has at most 512 chunks).
+// The per-key passes run only in waves that hold keys of the row.
+template <int KPT>
+__device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a, int row, int n, int32_t *out,
+                                                  const float *src) {
+    static_assert(kCandList % KPT == 0 || KPT % kCandList == 0, "whole lists or whole parts of one");
+    static_assert(KPT % 4 == 0, "whole 16-byte loads");
+    const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int k = a.k;
+    const int nch = (n + kCandChunk - 1) / kCandChunk;
+    const int nkeys = nch * kCandList;
+    const int nw = (n + 31) >> 5;
+    uint32_t *bits = sh.keys;  // [nw] kept columns
+    const bool wave_has = w * 64 * KPT < nkeys;  // uniform: this wave holds keys of the row
+    const int s0 = KPT * t;                     // first key slot of this thread
+    auto col_of = [](int slot, uint32_t kk) { return (slot / kCandList) * kCandChunk + 63 - (int)(kk & 63u); };
+
+    // ---- 1. keys, range, count -----------------------------------------------
+    uint32_t key[KPT];
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu, nf = 0u;
+    int nvalid = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = 0u;
+    if (wave_has) {
+        const uint4 *lp = reinterpret_cast<const uint4 *>(a.cand + (int64_t)row * a.cand_chunks * kCandList) +
+                          (s0 < nkeys ? s0 / 4 : 0);
+#pragma unroll
+        for (int q = 0; q < KPT / 4; ++q) {
+            const uint4 v = s0 + 4 * q < nkeys ? lp[q] : make_uint4(0u, 0u, 0u, 0u);
+            key[4 * q] = v.x;
+            key[4 * q + 1] = v.y;
+            key[4 * q + 2] = v.z;
+            key[4 * q + 3] = v.w;
+        }
+        // Only the row's last chunk has columns past n (its list then holds
+        // keys 0 or columns past n): the keys of the other chunks are all valid.
+        if (s0 + KPT > (nch - 1) * kCandList) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const uint32_t kk = key[j];
+                const bool valid = s0 + j < nkeys && kk != 0u && col_of(s0 + j, kk) < n;
+                key[j] = valid ? kk : 0u;
+                nvalid += valid ? 1 : 0;
+                kmax = valid ? max(kmax, kk) : kmax;
+                kmin = valid ? min(kmin, kk) : kmin;
+            }
+        } else {
+            nvalid = KPT;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                kmax = max(kmax, key[j]);
+                kmin = min(kmin, key[j]);
+            }
+        }
+        // a key at or above +inf's (or at or below -inf's) holds a non-finite score
+        nf = (nvalid > 0 && (kmax >= 0xFF800000u || kmin <= 0x007FFFFFu)) ? 1u : 0u;
+        kmax = nf ? 0u : kmax;
+        kmin = nf ? 0xFFFFFFFFu : kmin;
+    }
+    for (int i = t; i < nw; i += kThreads) bits[i] = 0u;
+    {
+        const int c = wave_total_sum(nvalid);
+        if (l == 0) sh.grp[w] = c;
+    }
+    if (t == 0) {
+        sh.ncand = 0;
+        sh.split_over = 0;
+    }
+    const RowRange rr = row_range(sh, kmax, kmin, nf, t);  // clears the histogram; barrier
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) total += sh.grp[i];
+    if (!rr.all_finite || total < k) return false;
+    const float sc = rr.scale, off = rr.vmax * rr.scale;
+
+    // ---- 2. histogram, crossing bucket, the k-th key ------------------------
+    // (buckets kept in registers for up to 16 keys, recomputed above that)
+    constexpr bool kKeepBuckets = KPT <= 16;
+    int bk[kKeepBuckets ? KPT : 1];
+    // the map reads a packed key as a float (its column bits move it by less
+    // than 64 ulp): monotone in the packed order, which is all it needs; keys
+    // below the range's low end (by those bits) clamp to the last bucket
+    auto bucket_of = [&](int j) {
+        if constexpr (kKeepBuckets) return bk[j];
+        else return fast_bucket(key_value(key[j]), sc, off);
+    };
+    if (wave_has) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int b = fast_bucket(key_value(key[j]), sc, off);
+            if constexpr (kKeepBuckets) bk[j] = b;
+            if (key[j]) atomicAdd(&sh.hist[b], 1u);
+        }
+    }
+    __syncthreads();
+    find_crossing(sh, k);
+    const int bstar = sh.cross_bin;
+    int need = k - sh.cross_above;
+    int cnt = sh.cross_cnt;
+    if (cnt > kCand) return false;
+    if (wave_has) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool hit = key[j] != 0u && bucket_of(j) == bstar;
+            const uint64_t m = ballot(hit);
+            if (m) {
+                const int lead = __builtin_ctzll(m);
+                int base = 0;
+                if (l == lead) base = atomicAdd(&sh.ncand, __popcll(m));
+                base = readlane(base, lead);
+                if (hit) sh.cand_key[base + mask_prefix(m)] = key[j];
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t P;
+    const int nc = sh.ncand;  // == cnt
+    if (nc <= 64) {  // keys are distinct: rank by key alone
+        if (w == 0) {
+            const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
+            int rank = 0;
+            for (int j = 0; j < nc; ++j) rank += ((uint32_t)readlane((int)mk, j) > mk) ? 1 : 0;
+            if (l < nc && rank == need - 1) sh.thr_key = mk;
+        }
+        __syncthreads();
+        P = sh.thr_key;
+    } else {
+        radix_select(sh, [&](auto f) {
+            for (int j = t; j < nc; j += kThreads) f(sh.cand_key[j]);
+        }, P, need, cnt);
+    }
+    __syncthreads();
+    if (t == 0) sh.ncand = 0;  // the tie group's count next
+    __syncthreads();
+
+    // ---- 3. kept keys, the tie group, lists that might miss columns ---------
+    const uint32_t tstar = P >> 6;
+    int above = 0;
+    bool sat = false;
+    if (wave_has) {
+        // smallest key of each list (or of this thread's part of its list)
+        constexpr int kParts = KPT < kCandList ? 1 : KPT / kCandList;
+        constexpr int kPartKeys = KPT < kCandList ? KPT : kCandList;
+        uint32_t lmin[kParts];
+#pragma unroll
+        for (int q = 0; q < kParts; ++q) lmin[q] = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t kk = key[j];
+            lmin[j / kPartKeys] = min(lmin[j / kPartKeys], kk);
+            const uint32_t tk = kk >> 6;
+            if (kk != 0u && tk >= tstar) {
+                const int col = col_of(s0 + j, kk);
+                if (tk > tstar) {
+                    atomicOr(&bits[col >> 5], 1u << (col & 31));
+                    ++above;
+                } else {
+                    const int at = atomicAdd(&sh.ncand, 1);
+                    if (at < kCandTies) sh.cand_col[at] = col;
+                }
+            }
+        }
+        // the 32nd key of each list: the smaller of its parts' minima
+        if constexpr (KPT < kCandList) {
+#pragma unroll
+            for (int m = 1; m < kCandList / KPT; m <<= 1) lmin[0] = min(lmin[0], (uint32_t)xor_lane_i((int)lmin[0], m));
+        }
+#pragma unroll
+        for (int q = 0; q < kParts; ++q) {
+            const int s = s0 + q * kPartKeys;
+            const int c = s / kCandList;
+            sat |= s < nkeys && n - kCandChunk * c > kCandList && (lmin[q] >> 6) >= tstar;
+        }
+    }
+    {
+        const int c = wave_total_sum(above);
+        const bool any_sat = ballot(sat) != 0ull;
+        if (l == 0) {
+            sh.grp[w] = c;
+            if (any_sat) sh.split_over = 1;
+        }
+    }
+    __syncthreads();
+    int nabove = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) nabove += sh.grp[i];
+    const int nt = sh.ncand;
+    const int need_t = k - nabove;
+    if (sh.split_over || nt > kCandTies || need_t < 1 || need_t > nt) return false;
+    if (w == 0) {
+        if (nt == 1) {  // P alone: it takes the last place
+            if (l == 0) {
+                const int mc = sh.cand_col[0];
+                atomicOr(&bits[mc >> 5], 1u << (mc & 31));
+            }
+        } else {  // rank the tie group on the exact logits: (value desc, column asc)
+            const int mc = l < nt ? sh.cand_col[l] : 0x7FFFFFFF;
+            const uint32_t mk = l < nt ? order_key(src[mc]) : 0u;
+            int rank = 0;
+            for (int j = 0; j < nt; ++j) {
+                const uint32_t kj = (uint32_t)readlane((int)mk, j);
+                const int cj = readlane(mc, j);
+                rank += (kj > mk || (kj == mk && cj < mc)) ? 1 : 0;
+            }
+            if (l < nt && rank < need_t) atomicOr(&bits[mc >> 5], 1u << (mc & 31));
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. the kept columns in order ----------------------------------------
+    const int per = (nw + kThreads - 1) / kThreads;
+    const int w0 = t * per;
+    int mine = 0;
+    for (int u = 0; u < per; ++u)
+        if (w0 + u < nw) mine += __popc(bits[w0 + u]);
+    const int incl = wave_incl_sum(mine);
+    if (l == 63) sh.wave_tot[w] = incl;
+    __syncthreads();
+    const int wt = l < kWaves ? sh.wave_tot[l] : 0;
+    const int wincl = wave_incl_sum(wt);
+    int p = readlane(wincl - wt, w) + incl - mine;
+    for (int u = 0; u < per; ++u) {
+        if (w0 + u >= nw) break;
+        uint32_t word = bits[w0 + u];
+        while (word) {
+            const int b = __builtin_ctz(word);
+            word &= word - 1u;
+            if (p < k) out[p] = 32 * (w0 + u) + b;
+            ++p;
+        }
+    }
+    return true;
+}
+
+// The full selection of one row, kept out of line: the fallback of the
+// selection from lists, called from one place so that the kernel's own code
+// stays small (each CU runs it once, from a cold instruction cache).
+__device__ __attribute__((noinline)) void select_full_row_cold(Shared &sh, const float *src, int n, int k,
+                                                                int32_t *out) {
+    select_full_row<true>(sh, src, n, k, out);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a) {
+    __shared__ Shared sh;
+    const int row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int k = a.k;
+    const int n = min(max(a.ctx_lens[row], 0), a.width);
+    int32_t *out = a.idx_out + (int64_t)row * k;
+    const float *src = a.logits + (int64_t)row * a.stride;
+    if (n <= k) {
+        for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    // past the table the logits are -inf and there are no candidates
+    if (n <= a.cap && select_from_lists<KPT>(sh, a, row, n, out, src)) return;
+    __syncthreads();
+    select_full_row_cold(sh, src, n, k, out);
+}
+
 }  // namespace
 
 int topk_groups_for_width(int width) { return width <= kMaxWidth ? 1 : 0; }
@@ -1458,6 +1749,20 @@ static void launch_split(const TopkArgs &a, hipStream_t s, hipEvent_t start, hip
     const unsigned g = (unsigned)a.num_rows * (unsigned)a.slices;
     hipExtLaunchKernelGGL(topk_window_kernel<G>, dim3(g), dim3(kThreads), 0, s, start, nullptr, 0, a);
     hipExtLaunchKernelGGL(topk_resolve_kernel<G>, dim3(g), dim3(kThreads), 0, s, nullptr, stop, 0, a);
+}
+
+hipError_t launch_topk_cand(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    if (a.num_rows == 0) return hipSuccess;
+    // keys per thread: 16 (half a list) for rows of up to 512 chunks (32,768
+    // columns), 32 up to 1,024 chunks, else 64
+    const int64_t keys = (int64_t)a.cand_chunks * kCandList;
+    if (keys <= 16 * kThreads)
+        hipExtLaunchKernelGGL(topk_cand_kernel<16>, dim3((unsigned)a.num_rows), dim3(kThreads), 0, s, start, stop, 0, a);
+    else if (keys <= 32 * kThreads)
+        hipExtLaunchKernelGGL(topk_cand_kernel<32>, dim3((unsigned)a.num_rows), dim3(kThreads), 0, s, start, stop, 0, a);
+    else
+        hipExtLaunchKernelGGL(topk_cand_kernel<64>, dim3((unsigned)a.num_rows), dim3(kThreads), 0, s, start, stop, 0, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {

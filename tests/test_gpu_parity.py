@@ -917,3 +917,149 @@ def test_select_score_topk_expand_decode_verify():
     gi = idx.cpu().numpy()
     assert_topk_exact(gi, oracle.topk(g.cpu().numpy(), inp.ctx_lens, inp.topk), label="select")
     assert np.array_equal(toks, oracle.expand(gi, 4, token_lens=tl))
+
+
+# ---------------------------------------------------------------------------
+# fused scoring + selection (qsa_paged_logits_topk)
+# ---------------------------------------------------------------------------
+
+def _fused_vs_two_calls(inp, label, workspace="auto"):
+    """The fused call's logits and indices against qsa_paged_logits followed by
+    qsa_topk (workspace "auto"), bit for bit, and its indices against the oracle's
+    selection on those same logits, exactly."""
+    m = qsa()
+    dev = to_device(inp)
+    R, W, k = inp.num_rows, inp.width, inp.topk
+    g1 = gpu_logits(inp, dev)
+    i1 = gpu_topk(g1, dev.ctx_lens, k)
+    g2, i2 = m.paged_logits_topk(dev.q, dev.kcache, dev.block_table, dev.ctx_lens, dev.row_to_req, k=k,
+                                 width=W, block_size=dev.block_size, w=dev.w, kscale=dev.kscale,
+                                 layout=dev.layout, workspace=workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g2), f"{label}: logits differ"
+    assert torch.equal(i1, i2), f"{label}: indices differ from the two calls"
+    x = g2.cpu().numpy()
+    assert_topk_exact(i2.cpu().numpy(), oracle.topk(x, inp.ctx_lens, k), label=label)
+    return g2, i2
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_verify", "decode_verify_fp16", "decode_verify_d64",
+                                  "single_row_mixed", "fp8_paged"])
+def test_fused_selection_workloads(name):
+    inp = qsa_inputs.make_config(name)
+    say("fused", name)
+    g, i = _fused_vs_two_calls(inp, f"fused {name}")
+    # and against the oracle's logits, end to end
+    o = oracle.paged_logits(inp)
+    tols = assert_logits_match(g.cpu().numpy(), o, inp, label=f"fused {name}")
+    oi = oracle.topk(o.astype(np.float32), inp.ctx_lens, inp.topk)
+    assert_topk_banded(i.cpu().numpy(), oi, o, tols, label=f"fused {name}")
+
+
+@pytest.mark.parametrize("H", [1, 2, 4])
+@pytest.mark.parametrize("B", [16, 64, 3])
+def test_fused_selection_shapes(H, B):
+    """Ragged visible counts from a few columns to many chunks: rows that fit in
+    k, short rows whose lists hold fewer than k keys (full-row selection), rows
+    near 3k..8k (many chunks reach the threshold: their other columns are added),
+    long rows; several rows per lane (H < 4), the per-column gather (B = 3),
+    weights, and a visible count past the table (the full-row selection)."""
+    k = 2048
+    ctx = [0, 5, k, k + 1, 3000, 5000, 6500, 8200, 12000, 16001, 20000, 24100, 30000, 2 * k + 7, 9999, 15000]
+    R = len(ctx)
+    # the width runs past the table (columns 30,000+ of every row are -inf)
+    inp = qsa_inputs.build(name="fused shapes", seed=40 + H + B, req_rows=[4] * (R // 4), ctx_rows=ctx,
+                           num_heads=H, block_size=B, weights=True, topk=k, width=32768)
+    say("fused shapes", H, B)
+    _fused_vs_two_calls(inp, f"fused H{H} B{B}")
+    # rows asking for more columns than the table holds (their selection reaches
+    # the -inf columns past it), and past the width
+    inp.ctx_lens = inp.ctx_lens.copy()
+    inp.ctx_lens[11] = inp.width + 500
+    inp.ctx_lens[12] = int(inp.max_blocks * inp.block_size) + 10
+    _fused_vs_two_calls(inp, f"fused H{H} B{B} ctx past the table")
+
+
+@pytest.mark.parametrize("kind", ["ties", "sorted", "spike"])
+def test_fused_selection_adversarial_scores(kind):
+    """Scores built to defeat the chunk lists: many equal scores (tie groups
+    wider than the exact-ranking wave), keys ordered so that the largest scores
+    crowd a few chunks (every list saturated), and one chunk holding far more
+    than 16 of the row's top columns."""
+    k = 2048
+    ctx = [24000, 30000, 18000, 9000, 24000, 30000, 18000, 9000]
+    inp = qsa_inputs.build(name="fused adv", seed=90, req_rows=[4, 4], ctx_rows=ctx, num_heads=4, block_size=16,
+                           topk=k)
+    B, D = inp.block_size, inp.head_dim
+    kc = inp.kcache.copy()
+    if kind == "ties":
+        # keys from a handful of patterns: many columns score exactly alike
+        pats = kc[:5].copy()
+        kc[:] = pats[np.arange(kc.shape[0]) % 5]
+    elif kind == "sorted":
+        # scale each key by its position in the request: scores grow with the column
+        for req in range(inp.num_reqs):
+            for c in range(int(inp.kv_lens[req])):
+                blk = inp.block_table[req, c // B]
+                f = np.float32(0.2 + 3.0 * c / 30000.0)
+                kc[blk, c % B] = qsa_inputs.f32_to_bf16_bits(
+                    (kc[blk, c % B].astype(np.uint32) << 16).view(np.float32) * f)
+    else:
+        # columns 640..1279 of every request get keys 8x larger
+        for req in range(inp.num_reqs):
+            for c in range(640, 1280):
+                blk = inp.block_table[req, c // B]
+                kc[blk, c % B] = qsa_inputs.f32_to_bf16_bits(
+                    (kc[blk, c % B].astype(np.uint32) << 16).view(np.float32) * np.float32(8.0))
+    inp.kcache = kc
+    say("fused adversarial", kind)
+    _fused_vs_two_calls(inp, f"fused {kind}")
+
+
+def test_fused_selection_without_workspace_and_in_a_graph():
+    """No workspace: the same results without fusion.  Captured in a HIP graph:
+    replays equal the eager call bit for bit, with other calls between them."""
+    m = qsa()
+    inp = qsa_inputs.make_config("decode_verify")
+    other = qsa_inputs.make_config("decode_verify", seed=55)
+    say("fused no workspace / graph")
+    _fused_vs_two_calls(inp, "fused no workspace", workspace=None)
+    dev, dev2 = to_device(inp), to_device(other)
+    s = torch.cuda.Stream()
+    out = torch.empty((inp.num_rows, inp.width), dtype=torch.float32, device="cuda")
+    idx = torch.empty((inp.num_rows, inp.topk), dtype=torch.int32, device="cuda")
+    out2 = torch.empty((other.num_rows, other.width), dtype=torch.float32, device="cuda")
+    idx2 = torch.empty((other.num_rows, other.topk), dtype=torch.int32, device="cuda")
+    call = m.PreparedLogitsTopk(dev.q, dev.kcache, dev.block_table, dev.ctx_lens, dev.row_to_req, out, idx,
+                                k=inp.topk, width=inp.width, block_size=inp.block_size, stream=s)
+    call2 = m.PreparedLogitsTopk(dev2.q, dev2.kcache, dev2.block_table, dev2.ctx_lens, dev2.row_to_req, out2, idx2,
+                                 k=other.topk, width=other.width, block_size=other.block_size, stream=s)
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    ref, ref_idx = out.clone(), idx.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(idx, ref_idx), f"replay {r}"
+        with torch.cuda.stream(s):
+            call2()
+        torch.cuda.synchronize()
+
+
+def test_fused_selection_widest_rows():
+    """Rows of up to 69,632 columns (two candidate lists per resolve thread)."""
+    ctx = [69632, 69000, 65600, 40000, 66000, 2049, 69632, 50000]
+    inp = qsa_inputs.build(name="fused wide", seed=97, req_rows=[4, 4], ctx_rows=ctx, num_heads=4, block_size=64,
+                           topk=2048, width=69632)
+    say("fused widest rows")
+    _fused_vs_two_calls(inp, "fused wide")
