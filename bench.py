@@ -11,14 +11,17 @@ input replicas that no step finds its keys in L2 or the 256 MB Infinity Cache
 (each replica's bytes are read again only after more than 512 MB of other
 traffic), except where one replica alone is larger than that.
 
-``value`` is microseconds per call (scoring + selection): HIP events around the
-K timed steps, nothing else in between.  ``roofline`` has one entry per kernel
-of the call (``kernels``: scoring, then top-k) and repeats the dominant one's
-figures at its top level: algorithmic bytes per launch / the mean duration of
-its launches, from a second pass over the same K steps in which every kernel
+``value`` is microseconds per call of the library's full call,
+qsa_paged_logits_topk (the logits written, then the top-k of them; on decode
+shapes the scoring epilogue feeds the selection): HIP events around the K timed
+steps, nothing else in between.  ``two_call_value`` times the same work as two
+calls (qsa_paged_logits, then qsa_topk).  ``roofline`` has one entry per kernel
+of the call (``kernels``: scoring, then selection) and repeats the dominant
+one's figures at its top level: algorithmic bytes per launch / the mean duration
+of its launches, from a third pass over the same K steps in which every kernel
 dispatch records a start and an end HIP event itself (on the stream the kernels
-run on), against the MI355X HBM peak of 8 TB/s; the prefill scorer also reports
-its MFMA rate against the dense bf16 peak.  ``configs`` summarises the same
+run on), against the MI355X HBM peak of 8 TB/s; the scorer also reports its MFMA
+rate against the dense peak of its dtype.  ``configs`` summarises the same
 figures for all five workloads (shorter runs).  ``cpu_baseline`` is the CPU
 oracle timed on this host's cores on a row sample of the headline workload.
 """
@@ -75,6 +78,8 @@ DESCRIPTIONS = {
                           "16x16-byte tiles: 16 requests x 4 rows, 64 heads, kv_len 32768, top-k 2048",
     "decode_verify_d64": "decode_verify with head dim 64: 9 requests x 4 MTP rows, 4 heads, D=64, bf16, "
                          "ctx U[16000,32000], block 16, top-k 2048",
+    "fp8_paged_ragged": "fp8_paged with 1..8 verify rows per request (63 rows over 16 requests): 64 heads, fp8, "
+                        "w U(0,1), kv_len 32768, co-packed KVB=64, top-k 2048",
 }
 
 
@@ -108,7 +113,8 @@ def scoring_kernel(inp):
     if (inp.dtype in ("bf16", "fp16") and inp.num_heads == 4 and inp.num_reqs == 1 and inp.num_rows >= 256
             and inp.block_size % 32 == 0):
         return "prefill_logits_kernel"
-    if inp.dtype == "fp8" and inp.num_heads in (32, 64) and inp.num_rows == 4 * inp.num_reqs:
+    if (inp.dtype == "fp8" and inp.num_heads in (32, 64) and inp.num_rows >= 2 * inp.num_reqs
+            and (inp.layout != "copacked_shuffled" or inp.block_size % 64 == 0)):
         return "mtp_fp8_kernel"
     if inp.dtype == "fp8" and inp.num_heads >= 16 and inp.block_size % 16 == 0:
         return "looped_logits_kernel"
@@ -359,11 +365,28 @@ def cpu_baseline(inp, budget_s=15.0):
                       f"scaled by rows; float64 C loops, OpenMP over rows on {threads} threads"}
 
 
+def _timed_region(step, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end)
+
+
 def measure(workload, steps, warmup):
-    """Time `steps` calls of the workload (after `warmup`), then the same steps
-    with every kernel timed by its own dispatch events.  Returns the figures of
-    one configuration (and the inputs)."""
-    import numpy as np  # noqa: F401
+    """Time `steps` calls of the workload (after `warmup`): the library's full
+    call (qsa_paged_logits_topk: scoring then selection, fused where the shape
+    allows), and the same work as two calls (qsa_paged_logits, qsa_topk) for
+    comparison; then the full calls again with the scoring and the selection
+    timed by their own dispatch events.  Returns the figures of one
+    configuration (and the inputs)."""
     import torch
 
     import paged_mqa_logits_block_amd as qsa
@@ -380,75 +403,73 @@ def measure(workload, steps, warmup):
     idx = torch.empty((inp.num_rows, inp.topk), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # calls validated once per replica; a step only crosses the C ABI twice
-    calls = []
+    # calls validated once per replica; a step only crosses the C ABI
+    full, two = [], []
     for d, o in zip(devs, outs):
-        calls.append((qsa.PreparedLogits(d.q, d.kcache, d.block_table, d.ctx_lens, d.row_to_req, o,
-                                         width=d.width, block_size=d.block_size, w=d.w,
-                                         kscale=d.kscale, layout=d.layout, stream=stream),
-                      qsa.PreparedTopk(o, d.ctx_lens, d.topk, idx, stream=stream)))
+        full.append(qsa.PreparedLogitsTopk(d.q, d.kcache, d.block_table, d.ctx_lens, d.row_to_req, o, idx,
+                                           k=d.topk, width=d.width, block_size=d.block_size, w=d.w,
+                                           kscale=d.kscale, layout=d.layout, stream=stream))
+        two.append((qsa.PreparedLogits(d.q, d.kcache, d.block_table, d.ctx_lens, d.row_to_req, o,
+                                       width=d.width, block_size=d.block_size, w=d.w, kscale=d.kscale,
+                                       layout=d.layout, stream=stream),
+                    qsa.PreparedTopk(o, d.ctx_lens, d.topk, idx, stream=stream)))
 
-    def step(i, evs=None):
-        lg, tk = calls[i % reps]
-        if evs is None:
-            lg()
-            tk()
-        else:
-            lg((evs[0], evs[1]))
-            tk((evs[2], evs[3]))
+    def step_full(i):
+        full[i % reps]()
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def step_two(i):
+        lg, tk = two[i % reps]
+        lg()
+        tk()
 
     # timed region: exactly K steps, events only around the whole region
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = _timed_region(step_full, steps, warmup, stream)
+    two_ms = _timed_region(step_two, steps, max(1, warmup // 2), stream)
 
-    # kernel durations: the same K steps again, each kernel timed by HIP events
-    # that its own dispatch records at kernel start and end (on the stream the
+    # kernel durations: the same K steps again, the scoring and the selection
+    # timed by HIP events that their own dispatches record (on the stream the
     # kernels run on); these events add host and GPU time per launch, so they
-    # stay out of the region above
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for e4 in evs:
-        for e in e4:
+    # stay out of the regions above
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e3 in evs:
+        for e in e3:
             e.record(stream)
     torch.cuda.synchronize()
     for i in range(steps):
-        step(i, evs[i])
+        full[i % reps](evs[i])
     torch.cuda.synchronize()
     logit_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
-    topk_us = statistics.mean(e[2].elapsed_time(e[3]) for e in evs) * 1e3
+    topk_us = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+    fused = full[0].workspace is not None and full[0].workspace.numel() > 0 and inp.num_heads <= 4 \
+        and scoring_kernel(inp) == "paged_logits_kernel"
 
     sk = scoring_kernel(inp)
     s_gbs = per_call / (logit_us * 1e-6) / 1e9
-    scoring = {"kernel": sk, "bound": "hbm", "us": round(logit_us, 2), "achieved": round(s_gbs, 1),
+    scoring = {"kernel": sk + (" (+ chunk candidates)" if fused else ""), "bound": "hbm",
+               "us": round(logit_us, 2), "achieved": round(s_gbs, 1),
                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(s_gbs / HBM_PEAK_GBS, 4),
-               "traffic": measured_traffic(workload, sk), "algorithmic_bytes": per_call,
+               "traffic": None if fused else measured_traffic(workload, sk), "algorithmic_bytes": per_call,
                "algorithmic_read_bytes": reads, "algorithmic_write_bytes": writes}
     flops = scoring_flops(inp)
     tflops = flops / (logit_us * 1e-6) / 1e12
     peak_tf = MFMA_PEAK_TFLOPS[inp.dtype]
     scoring["mfma"] = {"achieved": round(tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
                        "frac": round(tflops / peak_tf, 4), "algorithmic_flops": flops,
-                       "busy_frac_counters": measured_mfma_busy(workload, sk)}
+                       "busy_frac_counters": None if fused else measured_mfma_busy(workload, sk)}
     tplan = topk_plan(inp)
     t_gbs = (tk_reads + tk_writes) / (topk_us * 1e-6) / 1e9
-    topk = {"kernel": "topk_window_kernel + topk_resolve_kernel" if tplan == "split" else "topk_rows_kernel",
-            "bound": "hbm", "us": round(topk_us, 2), "achieved": round(t_gbs, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(t_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(workload, "topk"),
+    tkname = ("topk_cand_kernel" if fused else
+              "topk_window_kernel + topk_resolve_kernel" if tplan == "split" else "topk_rows_kernel")
+    topk = {"kernel": tkname, "bound": "hbm", "us": round(topk_us, 2), "achieved": round(t_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(t_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if fused else measured_traffic(workload, "topk"),
             "algorithmic_bytes": tk_reads + tk_writes, "algorithmic_read_bytes": tk_reads,
             "algorithmic_write_bytes": tk_writes}
     res = {"workload": workload, "value": round(total_ms * 1e3 / steps, 2), "ms_per_step": total_ms / steps,
+           "two_call_value": round(two_ms * 1e3 / steps, 2), "fused": fused,
            "logits_us": round(logit_us, 2), "topk_us": round(topk_us, 2), "scoring": scoring, "topk": topk,
            "replicas": reps, "steps": steps, "warmup": warmup}
-    del calls, devs, outs, idx
+    del full, two, devs, outs, idx
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res, inp
@@ -531,13 +552,16 @@ def main():
                    "block": inp.block_size, "topk": inp.topk, "input_replicas": head["replicas"]},
         "logits_us": head["logits_us"],
         "topk_us": head["topk_us"],
+        "two_call_value": head["two_call_value"],
+        "fused_selection": head["fused"],
         "roofline": roofline,
     }
     if not args.no_configs:
         summary = []
         for name in qsa_inputs.CONFIG_NAMES:
             r = head if name == args.workload else measure(name, args.config_steps, 5)[0]
-            summary.append({"workload": name, "value": r["value"], "logits_us": r["logits_us"],
+            summary.append({"workload": name, "value": r["value"], "two_call_value": r["two_call_value"],
+                            "fused_selection": r["fused"], "logits_us": r["logits_us"],
                             "topk_us": r["topk_us"], "scoring_kernel": r["scoring"]["kernel"],
                             "scoring_frac": r["scoring"]["frac"],
                             "scoring_mfma_frac": r["scoring"]["mfma"]["frac"],

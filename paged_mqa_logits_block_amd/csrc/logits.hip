@@ -15,16 +15,17 @@ LogitsPlan plan_logits(int dtype, int layout, int head_dim, int num_heads, int n
     // the looped, 4-row and prefill kernels are built for D = 128; other head
     // dims take the per-tile kernel
     const bool d128 = head_dim == 128;
-    // fp8, 32 or 64 heads, 4 rows per request on average (MTP verify): 4-row
-    // workgroups sharing each key run (any block size for block-flat keys,
-    // whole 64-column runs per block for preshuffled ones); chunks sized for
-    // about four workgroups per CU
-    if (d128 && dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows == 4 * num_reqs &&
+    // fp8, 32 or 64 heads, 2 or more rows per request on average (MTP verify,
+    // ragged included): 4-row workgroups sharing each key run (a tile whose
+    // rows belong to several requests walks them one at a time; any block
+    // size for block-flat keys, whole 64-column runs per block for preshuffled
+    // ones); chunks sized for about four workgroups per CU
+    if (d128 && dtype == kFP8 && (num_heads == 32 || num_heads == 64) && num_reqs > 0 && num_rows >= 2 * num_reqs &&
         (layout != 2 || block_size % kMtpRunCols == 0)) {
         p.mtp = true;
         p.rows_per_tile = 4;
         p.m_tiles = num_heads / 16;
-        const int row_tiles = num_rows / 4;
+        const int row_tiles = (num_rows + 3) / 4;
         const int runs = (width + kMtpRunCols - 1) / kMtpRunCols;
         int per = 1;
         while (per < kMtpMaxRunsPerGroup && (int64_t)row_tiles * ((runs + per - 1) / per) > 1024) per *= 2;

@@ -53,6 +53,8 @@ KVB1_CONFIG_NAMES = ("fp8_paged_kvb1",)
 SHUFFLED_CONFIG_NAMES = ("fp8_paged_shuffled",)
 # decode_verify with head dim 64
 D64_CONFIG_NAMES = ("decode_verify_d64",)
+# fp8_paged with a ragged number of verify rows per request (1..8, mean 4.5)
+RAGGED_CONFIG_NAMES = ("fp8_paged_ragged",)
 
 
 @dataclasses.dataclass
@@ -286,7 +288,8 @@ def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> 
     """The five named workloads, seeded 1..5 by default; fp16 variants of
     decode_verify and prefill_chunk (same shapes and recipe, seeds 6 and 7);
     fp8_paged with one key per block (seed 8); fp8_paged with preshuffled keys
-    (seed 9); decode_verify with head dim 64 (seed 10)."""
+    (seed 9); decode_verify with head dim 64 (seed 10); fp8_paged with 1..8 verify
+    rows per request (seed 11)."""
     if name == "fp8_paged_kvb1":
         kv_len, next_n, reqs = 32768, 4, 16
         ctx = [kv_len - next_n + n + 1 for _ in range(reqs) for n in range(next_n)]
@@ -300,6 +303,17 @@ def make_config(name: str, seed: Optional[int] = None, poison: bool = False) -> 
         return build(name=name, seed=9 if seed is None else seed, req_rows=[next_n] * reqs,
                      ctx_rows=ctx, kv_lens=[kv_len] * reqs, num_heads=64, block_size=64,
                      dtype="fp8", layout="copacked_shuffled", weights=True, max_blocks=512,
+                     width=32768, topk=2048, poison=poison)
+    if name == "fp8_paged_ragged":
+        # confidence-trimmed MTP verify: next_n drawn per request from 1..8
+        # (mean 4.5); row n of a request sees kv_len - next_n + n + 1 columns
+        rng = np.random.default_rng(11 if seed is None else seed)
+        kv_len, reqs = 32768, 16
+        next_n = rng.integers(1, 9, size=reqs)
+        ctx = [kv_len - int(nn) + n + 1 for nn in next_n for n in range(int(nn))]
+        return build(name=name, seed=int(rng.integers(1 << 31)), req_rows=[int(x) for x in next_n],
+                     ctx_rows=ctx, kv_lens=[kv_len] * reqs, num_heads=64, block_size=64,
+                     dtype="fp8", layout="copacked", weights=True, max_blocks=512,
                      width=32768, topk=2048, poison=poison)
     if name == "decode_verify_d64":
         rng = np.random.default_rng(10 if seed is None else seed)

@@ -59,7 +59,7 @@ SAMPLED_ROWS["prefill_chunk_fp16"] = SAMPLED_ROWS["prefill_chunk"]
 
 @pytest.mark.parametrize("name", qsa_inputs.CONFIG_NAMES + qsa_inputs.FP16_CONFIG_NAMES +
                          qsa_inputs.KVB1_CONFIG_NAMES + qsa_inputs.SHUFFLED_CONFIG_NAMES +
-                         qsa_inputs.D64_CONFIG_NAMES)
+                         qsa_inputs.D64_CONFIG_NAMES + qsa_inputs.RAGGED_CONFIG_NAMES)
 def test_config_logits_and_topk(name):
     inp = qsa_inputs.make_config(name, poison=True)
     rows = SAMPLED_ROWS.get(name)
@@ -114,7 +114,7 @@ def test_heads_and_dtypes(H, dtype, layout):
 
 @pytest.mark.parametrize("H", [16, 32, 64])
 @pytest.mark.parametrize("layout", ["paged", "copacked"])
-@pytest.mark.parametrize("req_rows", [(4, 4, 4, 4), (5, 3, 6, 2)])
+@pytest.mark.parametrize("req_rows", [(4, 4, 4, 4), (5, 3, 6, 2), (7, 8, 1, 3), (8, 8, 2)])
 def test_fp8_many_heads_mtp_rows(H, layout, req_rows):
     """fp8, 16+ heads, 4+ rows per request (the MTP verify shape): ragged ctx
     within a request, requests of unequal row counts, a width that ends inside
