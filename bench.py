@@ -105,7 +105,7 @@ def scoring_kernel(inp):
     """The scoring kernel the library picks for this shape (the same rule as
     its planner): the prefill variant for bf16 or fp16, 4 heads and one request with
     256+ rows and blocks of a multiple of 32 columns; the 4-row variant for fp8
-    with 32/64 heads and 4 rows per request; the looped variant for other fp8
+    with 32/64 heads and 2+ rows per request on average; the looped variant for other fp8
     shapes with 16+ heads and blocks of a multiple of 16 columns; the per-tile
     variant otherwise."""
     if inp.head_dim != 128:

@@ -167,7 +167,8 @@ qsa::LogitsArgs logits_args(const void *q, const float *w, const void *kcache, c
     a.width = s->width;
     const int64_t table_cols = (int64_t)s->max_blocks * s->block_size;
     a.cap = (int32_t)(table_cols < s->width ? table_cols : s->width);
-    a.num_row_tiles = (s->num_rows + plan.rows_per_tile - 1) / plan.rows_per_tile;
+    a.num_row_tiles = plan.mtp ? plan.row_tiles : (s->num_rows + plan.rows_per_tile - 1) / plan.rows_per_tile;
+    a.mtp_aligned = plan.mtp && plan.mtp_aligned;
     const int chunk_cols = 16 * plan.tiles_per_prog;
     a.num_chunks = (s->width + chunk_cols - 1) / chunk_cols;
     a.dtype = s->k_dtype;

@@ -12,6 +12,7 @@ LogitsPlan plan_logits(int dtype, int layout, int head_dim, int num_heads, int n
     p.iters = 0;
     p.prefill = false;
     p.mtp = false;
+    p.mtp_aligned = false;
     // the looped, 4-row and prefill kernels are built for D = 128; other head
     // dims take the per-tile kernel
     const bool d128 = head_dim == 128;
@@ -25,7 +26,17 @@ LogitsPlan plan_logits(int dtype, int layout, int head_dim, int num_heads, int n
         p.mtp = true;
         p.rows_per_tile = 4;
         p.m_tiles = num_heads / 16;
-        const int row_tiles = (num_rows + 3) / 4;
+        // Tiles of up to 4 consecutive rows of one request when the rows per
+        // request may differ (R != 4 * reqs, at most kMtpAlignedMaxRows rows):
+        // a request's rows are cut into tiles of 4 from its first row, so a
+        // tile never walks two requests.  Rows grouped by request make at most
+        // sum ceil(n_i / 4) <= (R + 3 min(reqs, R)) / 4 tiles; the kernel takes
+        // plain tiles when the rows make more (grouped otherwise).  R = 4 * reqs
+        // is taken as 4 rows per request, where plain tiles are the same.
+        p.mtp_aligned = num_rows <= kMtpAlignedMaxRows && num_rows != 4 * num_reqs;
+        const int row_tiles =
+            p.mtp_aligned ? min(num_rows, (num_rows + 3 * min(num_reqs, num_rows)) / 4) : (num_rows + 3) / 4;
+        p.row_tiles = row_tiles;
         const int runs = (width + kMtpRunCols - 1) / kMtpRunCols;
         int per = 1;
         while (per < kMtpMaxRunsPerGroup && (int64_t)row_tiles * ((runs + per - 1) / per) > 1024) per *= 2;

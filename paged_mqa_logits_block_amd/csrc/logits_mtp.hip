@@ -16,6 +16,18 @@ namespace {
 // the waits on the key fetches stay exact (loads and stores share one counter
 // on gfx9).  A tile whose rows belong to several requests walks them one at a
 // time; the waves whose row is not in the current request skip the scoring.
+//
+// Tiles: 4 consecutive rows each, or, when the planner asks for it (at most
+// kMtpAlignedMaxRows rows), tiles that follow the requests: a segment (a
+// maximal run of consecutive rows of one request) is cut into tiles of 4 rows
+// from its first row, and tiles are numbered in row order.  Every workgroup
+// finds the tile starts itself (thread t stands for row t: a max-scan of the
+// segments' first rows, then a count of the starts before it), so a ragged
+// number of rows per request (1..8 verify rows) costs one key pass per tile
+// instead of one per request that a tile touches.  The grid holds as many tiles
+// as rows grouped by request can need; when the rows come in another order and
+// make more tiles than that, every workgroup takes the plain 4-row tile instead
+// (the grid always holds those), so every row is covered whatever the order.
 constexpr int kMtpRun = kMtpRunCols;          // columns per run
 constexpr int kMtpKeyLds = 144;               // padded key in LDS (bytes)
 constexpr int kMtpDepth = 4;                  // runs in flight
@@ -44,18 +56,51 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
     const int l = lane_id();
     const int g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave = row of the tile
-    const int tile = blockIdx.x / a.num_chunks;
-    const int chunk = blockIdx.x - tile * a.num_chunks;
+    const int chunk = blockIdx.x % a.num_chunks;
     const int ncols = kMtpRun * a.iters;
     const int c0 = chunk * ncols;
-    const int row = tile * 4 + w;
+
+    // the tile's first row and its row count
+    const int tile = blockIdx.x / a.num_chunks;
+    int trow0 = tile * 4, tn = min(4, a.num_rows - trow0);
+    if (a.mtp_aligned) {
+        __shared__ int tmax[4], tcnt[4], tsel[2];
+        const bool in = t < a.num_rows;
+        const int rq = in ? a.row_to_req[t] : 0;
+        const int rp = (in && t > 0) ? a.row_to_req[t - 1] : rq;
+        const bool first = in && (t == 0 || rq != rp);
+        int ss = wave_scan_dpp(first ? t : 0, 0, OpMaxI());  // first row of t's segment (within the wave)
+        if (l == 63) tmax[w] = ss;
+        __syncthreads();
+        for (int u = 0; u < w; ++u) ss = max(ss, tmax[u]);
+        const bool st = in && ((t - ss) & 3) == 0;
+        const uint64_t b = ballot(st);
+        if (l == 0) tcnt[w] = __popcll(b);
+        __syncthreads();
+        const int ntiles = tcnt[0] + tcnt[1] + tcnt[2] + tcnt[3];
+        // more tiles than the grid holds (rows not grouped by request): plain
+        // tiles of 4 rows, which cover every row in any order
+        if (ntiles <= a.num_row_tiles) {
+            if (tile >= ntiles) return;
+            int off = 0;
+            for (int u = 0; u < w; ++u) off += tcnt[u];
+            const int k = st ? off + mask_prefix(b) : -1;  // number of the tile starting at row t
+            if (k == tile) tsel[0] = t;
+            if (k == tile + 1) tsel[1] = t;
+            __syncthreads();
+            trow0 = tsel[0];
+            tn = (tile + 1 < ntiles ? tsel[1] : a.num_rows) - trow0;
+        }
+    }
+    if (tn <= 0) return;
+    const int row = trow0 + w;
 
     // the tile's rows: visible counts and requests (every wave reads all 4)
     int ctx_r[4], req_r[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int rr = min(tile * 4 + r, a.num_rows - 1);
-        const bool valid = tile * 4 + r < a.num_rows;
+        const int rr = min(trow0 + r, a.num_rows - 1);
+        const bool valid = r < tn;
         ctx_r[r] = valid ? min(max(a.ctx_lens[rr], 0), a.cap) : 0;
         req_r[r] = valid ? a.row_to_req[rr] : -1;
     }
@@ -86,9 +131,7 @@ __global__ __launch_bounds__(256, 4) void mtp_fp8_kernel(LogitsArgs a) {
     const int lane_key_lds = (t >> 2) * kMtpKeyLds + 32 * (t & 3);
     const int frag = (l & 15) * kMtpKeyLds + F::lane_bytes(l);
 
-    uint32_t todo = 0u;  // tile rows not yet handled
-#pragma unroll
-    for (int r = 0; r < 4; ++r) todo |= (tile * 4 + r < a.num_rows ? 1u : 0u) << r;
+    uint32_t todo = (1u << tn) - 1u;  // tile rows not yet handled
     while (todo) {
         const int r0 = __builtin_ctz(todo);
         int req = 0;

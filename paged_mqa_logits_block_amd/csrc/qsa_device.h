@@ -111,6 +111,9 @@ __device__ __forceinline__ int wave_scan_dpp(int v, int identity, Op op) {
 struct OpAdd {
     __device__ __forceinline__ int operator()(int a, int b) const { return a + b; }
 };
+struct OpMaxI {
+    __device__ __forceinline__ int operator()(int a, int b) const { return max(a, b); }
+};
 struct OpMaxU {
     __device__ __forceinline__ int operator()(int a, int b) const {
         return (int)max((uint32_t)a, (uint32_t)b);

@@ -39,6 +39,8 @@ struct LogitsArgs {
     int64_t scale_offset;   // co-packed: byte offset of the scales inside a block
     int32_t iters;          // looped variant: key-tile groups per program
     int32_t pad2_;
+    int32_t mtp_aligned;    // 4-row fp8 variant: tiles follow the requests (see logits_mtp.hip)
+    int32_t pad3_;
     uint32_t *cand;         // or null: the per-tile kernel also writes each row's chunk candidates
                             // ([rows][num_chunks][32] packed keys) for the fused selection
 };
@@ -52,11 +54,16 @@ struct LogitsPlan {
                          // (prefill variant: 32-column steps per program)
     bool prefill;        // prefill variant (bf16, 4 heads, one request)
     bool mtp;            // 4-row fp8 variant (32/64 heads; iters = 64-column runs per program)
+    bool mtp_aligned;    // its tiles follow the requests (row tiles: an upper bound of their count)
+    int row_tiles;       // row tiles of the grid
 };
 
-// 4-row fp8 variant: columns per key run, runs per program at most
+// 4-row fp8 variant: columns per key run, runs per program at most, and the
+// most rows for which its tiles follow the requests (each workgroup finds its
+// tile by scanning row_to_req)
 constexpr int kMtpRunCols = 64;
 constexpr int kMtpMaxRunsPerGroup = 16;
+constexpr int kMtpAlignedMaxRows = 256;
 
 // consumer waves per workgroup of the prefill variant (16 rows each; one
 // producer wave besides), and how many of its workgroups one CU holds at once

@@ -152,6 +152,38 @@ def test_fp8_four_row_requests(H, layout, shuffle):
     assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"mtp4 H{H}")
 
 
+@pytest.mark.parametrize("reqs,B,layout,shuffle", [
+    (40, 64, "copacked", False),    # ~180 rows grouped by request: tiles follow the requests
+    (40, 128, "copacked_shuffled", False),
+    (40, 3, "paged", False),        # the same with blocks of 3 columns (gather)
+    (40, 64, "copacked", True),     # rows scattered: more tiles than the grid holds, plain tiles
+    (57, 64, "paged", False),       # exactly 256 rows
+    (70, 64, "copacked", False),    # past 256 rows: plain tiles walking the requests
+])
+def test_fp8_ragged_verify_rows(reqs, B, layout, shuffle):
+    """fp8, 64 heads, 1..8 verify rows per request (ragged next_n): the 4-row
+    variant with tiles cut from each request's first row, its fallback to plain
+    tiles for rows not grouped by request, and plain tiles past 256 rows."""
+    rng = np.random.default_rng(900 + reqs + B)
+    if reqs == 57:
+        counts = np.array([5] * 32 + [1] * 4 + [5] * 8 + [4] * 13)
+        assert counts.sum() == 256
+    else:
+        counts = rng.integers(1, 9, size=reqs)
+    n = int(counts.sum())
+    # row j of a request with nn rows and kv_len keys sees kv_len - nn + j + 1
+    ctx = []
+    for nn in counts:
+        kv_len = int(rng.integers(1, 3005))
+        ctx += [max(kv_len - int(nn) + j + 1, 0) for j in range(int(nn))]
+    inp = qsa_inputs.build(name="ragged", seed=950 + reqs + B, req_rows=[int(c) for c in counts],
+                           ctx_rows=ctx, num_heads=64, block_size=B, dtype="fp8",
+                           layout=layout, weights=True, width=3004, poison=True, shuffle_rows=shuffle)
+    say("fp8 ragged rows", reqs, n, B, layout, "shuffle", shuffle)
+    _, g = run_logits(inp)
+    assert_logits_match(g.cpu().numpy(), oracle.paged_logits(inp), inp, label=f"ragged R{n} B{B}")
+
+
 @pytest.mark.parametrize("B", [1, 3, 100])
 @pytest.mark.parametrize("H,layout", [(64, "copacked"), (32, "paged")])
 @pytest.mark.parametrize("shuffle", [False, True])
