@@ -203,13 +203,45 @@ def _matches(kernel, name):
     return base.startswith("topk_") if kernel == "topk" else base.startswith(kernel)
 
 
+def _template_args(name):
+    """The template argument list of a dispatch's kernel name, as strings."""
+    base = name.removeprefix("void ")
+    if base.endswith(")"):
+        base = base[:base.rindex("(")]
+    if "<" not in base:
+        return []
+    return [a.strip() for a in base[base.index("<") + 1:base.rindex(">")].split(",")]
+
+
+def _value_path(kernel, names):
+    """The kernels of the call that `value` times, among the dispatched names:
+    a run that also timed the fused scoring + selection (topk_cand_kernel
+    dispatched) times it as `value`, so only its kernels count -- the per-tile
+    scorer with the candidate epilogue (last template argument true) and the
+    candidate selection; the two-call path's kernels of the same run do not."""
+    fused = any(_matches("topk_cand_kernel", n) for n in names)
+    if not fused:
+        return set(names)
+    keep = set()
+    for n in names:
+        if kernel == "topk":
+            if _matches("topk_cand_kernel", n):
+                keep.add(n)
+        elif not _matches("paged_logits_kernel", n) or _template_args(n)[-1:] == ["true"]:
+            keep.add(n)
+    return keep
+
+
 def _per_call(kernel, rows):
     """Mean counter value per call: the mean over each matching kernel's
-    dispatches, summed over the kernels of a call (the split top-k runs two)."""
+    dispatches, summed over the kernels of a call (the split top-k runs two);
+    with the fused call in the run, only its kernels."""
     by = {}
     for k, v in rows:
         if _matches(kernel, k):
             by.setdefault(k, []).append(v)
+    names = _value_path(kernel, [k for k, _ in rows])
+    by = {k: v for k, v in by.items() if k in names}
     if not by:
         return None, 0, ""
     return (sum(statistics.mean(v) for v in by.values()), min(len(v) for v in by.values()),
@@ -448,21 +480,21 @@ def measure(workload, steps, warmup):
     scoring = {"kernel": sk + (" (+ chunk candidates)" if fused else ""), "bound": "hbm",
                "us": round(logit_us, 2), "achieved": round(s_gbs, 1),
                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(s_gbs / HBM_PEAK_GBS, 4),
-               "traffic": None if fused else measured_traffic(workload, sk), "algorithmic_bytes": per_call,
+               "traffic": measured_traffic(workload, sk), "algorithmic_bytes": per_call,
                "algorithmic_read_bytes": reads, "algorithmic_write_bytes": writes}
     flops = scoring_flops(inp)
     tflops = flops / (logit_us * 1e-6) / 1e12
     peak_tf = MFMA_PEAK_TFLOPS[inp.dtype]
     scoring["mfma"] = {"achieved": round(tflops, 1), "peak": peak_tf, "unit": "TFLOP/s",
                        "frac": round(tflops / peak_tf, 4), "algorithmic_flops": flops,
-                       "busy_frac_counters": None if fused else measured_mfma_busy(workload, sk)}
+                       "busy_frac_counters": measured_mfma_busy(workload, sk)}
     tplan = topk_plan(inp)
     t_gbs = (tk_reads + tk_writes) / (topk_us * 1e-6) / 1e9
     tkname = ("topk_cand_kernel" if fused else
               "topk_window_kernel + topk_resolve_kernel" if tplan == "split" else "topk_rows_kernel")
     topk = {"kernel": tkname, "bound": "hbm", "us": round(topk_us, 2), "achieved": round(t_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(t_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if fused else measured_traffic(workload, "topk"),
+            "traffic": measured_traffic(workload, "topk"),
             "algorithmic_bytes": tk_reads + tk_writes, "algorithmic_read_bytes": tk_reads,
             "algorithmic_write_bytes": tk_writes}
     res = {"workload": workload, "value": round(total_ms * 1e3 / steps, 2), "ms_per_step": total_ms / steps,

@@ -92,3 +92,35 @@ def test_write_mfma_busy_fraction(tmp_path, monkeypatch):
             wr.writerow({"Dispatch_Id": i // 2, "Kernel_Name": full, "Counter_Name": c, "Counter_Value": v})
     bench.write_mfma("prefill_chunk", k, str(folder))
     assert bench.measured_mfma_busy("prefill_chunk", k) == 0.4
+
+
+def test_write_traffic_counts_only_the_fused_call(tmp_path, monkeypatch):
+    """A run that times the fused scoring + selection as its value also runs the
+    two-call path: only the fused call's kernels (the scorer with the candidate
+    epilogue, the candidate selection) count, not both scorers summed."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    plain = "void qsa::(anonymous namespace)::paged_logits_kernel<0, 4, 1, 4, false, false, false, 128, false>(qsa::LogitsArgs)"
+    cand = "void qsa::(anonymous namespace)::paged_logits_kernel<0, 4, 1, 4, false, false, false, 128, true>(qsa::LogitsArgs)"
+    sel = "void qsa::(anonymous namespace)::topk_cand_kernel<16>(qsa::TopkArgs)"
+    win = "void qsa::(anonymous namespace)::topk_window_kernel<2>(qsa::TopkArgs)"
+    res = "void qsa::(anonymous namespace)::topk_resolve_kernel<2>(qsa::TopkArgs)"
+    write_csv(tmp_path / "cf", "FETCH_SIZE", [("copy", 524288.0)])
+    write_csv(tmp_path / "cw", "WRITE_SIZE", [("copy", 1048576.0)])
+    rows = [(cand, 100.0), (sel, 5.0), (plain, 90.0), (win, 7.0), (res, 9.0)] * 2
+    write_csv(tmp_path / "f", "FETCH_SIZE", rows)
+    write_csv(tmp_path / "w", "WRITE_SIZE", rows)
+    dirs = [str(tmp_path / d) for d in ("f", "w", "cf", "cw")]
+    bench.write_traffic("decode_verify", "paged_logits_kernel", dirs, 1024)
+    bench.write_traffic("decode_verify", "topk", dirs, 1024)
+    t = json.load(open(tmp_path / "traffic.json"))
+    assert t["decode_verify"]["fetch_bytes"] == 100 * 1024 * 2
+    assert t["decode_verify"]["kernel"].endswith("128, true>")
+    assert t["decode_verify:topk"]["fetch_bytes"] == 5 * 1024 * 2
+    assert t["decode_verify:topk"]["kernel"].endswith("topk_cand_kernel<16>")
+    # without the fused call in the run, every matching kernel of the call counts
+    rows2 = [(plain, 90.0), (win, 7.0), (res, 9.0)]
+    write_csv(tmp_path / "f2", "FETCH_SIZE", rows2)
+    write_csv(tmp_path / "w2", "WRITE_SIZE", rows2)
+    dirs2 = [str(tmp_path / d) for d in ("f2", "w2", "cf", "cw")]
+    bench.write_traffic("fp8_paged", "topk", dirs2, 1024)
+    assert json.load(open(tmp_path / "traffic.json"))["fp8_paged:topk"]["fetch_bytes"] == 16 * 1024 * 2
