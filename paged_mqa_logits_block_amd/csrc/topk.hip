@@ -760,24 +760,37 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     const float Tf = key_value(T);
 
     // ---- the kept set in column order, through LDS -----------------------
+    // Each float4 group's kept flags go to LDS as one byte (group i: byte i,
+    // columns 4i .. 4i+3 in its low 4 bits); thread t then ranks columns
+    // 32t .. 32t+31 from two words of that byte array: popcounts, a wave scan
+    // and one scan of the wave totals give its first place in the kept list.
     uint32_t sel = 0u;
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sel |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << (4 * j + e);
-    static_assert(kStageGroups == kChunk, "one ranking round covers the row");
-    int offs[kChunk];
-    chunk_ranks(sh, sel, offs);
-    uint32_t *kept = sh.cand_key;  // k <= kCand column indices, in order (the members are no longer needed)
+    static_assert(kStageGroups * kThreads <= (int)sizeof(int) * kCand, "a byte per group fits cand_col");
+    uint8_t *flags = reinterpret_cast<uint8_t *>(sh.cand_col);  // the members are no longer needed
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-        int p = offs[j];
+    for (int j = 0; j < kStageGroups; ++j) flags[t + kThreads * j] = (uint8_t)((sel >> (4 * j)) & 0xFu);
+    __syncthreads();
+    const uint2 fw = reinterpret_cast<const uint2 *>(flags)[t];  // groups 8t .. 8t+7
+    const int mine = __popc(fw.x) + __popc(fw.y);
+    const int incl = wave_incl_sum(mine);
+    if (l == 63) sh.wave_tot[w] = incl;
+    __syncthreads();
+    const int wt = l < kWaves ? sh.wave_tot[l] : 0;
+    const int wincl = wave_incl_sum(wt);
+    int p = readlane(wincl - wt, w) + incl - mine;
+    uint32_t *kept = sh.cand_key;  // k <= kCand column indices, in order
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if ((sel >> (4 * j + e)) & 1u) {
-                if (p < k) kept[p] = (uint32_t)(4 * (t + kThreads * j) + e);
-                ++p;
-            }
+    for (int h = 0; h < 2; ++h) {
+        uint32_t word = h ? fw.y : fw.x;  // bit 8b + e: column 32t + 16h + 4b + e
+        while (word) {
+            const int b = __builtin_ctz(word);
+            word &= word - 1u;
+            if (p < k) kept[p] = (uint32_t)(32 * t + 16 * h + 4 * (b >> 3) + (b & 7));
+            ++p;
         }
     }
     __syncthreads();
