@@ -669,6 +669,7 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], sc, off)], e < tail ? 1u : 0u);
         }
     }
+    if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
     __syncthreads();
     find_crossing(sh, k);
     const int bstar = sh.cross_bin;
@@ -680,8 +681,6 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     }
 
     // ---- the members of the crossing bucket, as (key, column) ------------
-    if (t == 0) sh.ncand = 0;
-    __syncthreads();
     // fast_bucket(v) == bstar exactly when the fma's f lies in [f_lo, f_hi)
     const float f_lo = bstar <= 1 ? -__builtin_inff() : (float)(bstar - 1);
     const float f_hi = bstar >= kBins - 2 ? __builtin_inff() : (float)bstar;
@@ -885,9 +884,12 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         const int nst = more ? start_of(nxt) : 0;
         const int nn = more ? visible(nxt, nst) : 0;
         const bool fast = fast_row(n, st);
+        // Every thread reads back only the slots its own lane copied, so the
+        // copy needs no barrier: the wave's wait covers its own copies, and the
+        // reads complete before the next copy into the same slots is issued.
+        // The kept columns were ordered by select_fast's last barrier.
         if (fast) {
             wait_dma();
-            __syncthreads();
             int tt = t;
             asm volatile("" : "+v"(tt));
 #pragma unroll
@@ -897,7 +899,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
             flush_kept(sh, k, pend);
             pend = nullptr;
         }
-        __syncthreads();  // pref and the kept columns have been read (the previous row is done with LDS)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (more && fast_row(nn, nst)) prefetch(nxt, nn, nst);
         int32_t *out = a.idx_out + (int64_t)row * k;
         if (n <= k) {
