@@ -51,6 +51,7 @@ constexpr int kBins = 2048;
 constexpr int kStage = 32768;    // longest row staged in LDS
 constexpr int kMaxWidth = 69632;
 constexpr int kCand = 2048;      // (key, column) list of the crossing bucket
+constexpr int kRankAll = 24;     // member lists this short are ranked by every wave
 constexpr int kChunk = 8;        // float4 groups ranked per compaction round
 constexpr int kStageGroups = kStage / 4 / kThreads;
 constexpr int kMaxGroups = (kMaxWidth + 4 * kThreads - 1) / (4 * kThreads);
@@ -155,6 +156,39 @@ __device__ __forceinline__ void find_crossing(Sh &sh, int need) {
         sh.cross_cnt = h1;
     }
     __syncthreads();
+}
+
+// find_crossing with one barrier, its result in every thread's registers: each
+// wave finds, from the waves' totals, the wave whose bins hold the crossing and
+// scans that wave's 128 bins itself.  All threads, fully active.
+struct Crossing {
+    int bin, above, cnt;
+};
+__device__ __forceinline__ Crossing find_crossing_w(Shared &sh, int need) {
+    const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int h0 = (int)sh.hist[2 * t], h1 = (int)sh.hist[2 * t + 1];
+    const int incl = wave_incl_sum(h0 + h1);
+    if (l == 63) sh.wave_tot[w] = incl;
+    __syncthreads();
+    const int wt = l < kWaves ? sh.wave_tot[l] : 0;
+    const int winc = wave_incl_sum(wt);
+    const int cw = __builtin_ctzll(ballot(l < kWaves && winc >= need) | (1ull << (kWaves - 1)));
+    const int before = readlane(winc - wt, cw);
+    const int b = 2 * (64 * cw + l);
+    const int g0 = (int)sh.hist[b], g1 = (int)sh.hist[b + 1];
+    const int ginc = wave_incl_sum(g0 + g1);
+    const int excl = before + ginc - g0 - g1;
+    const bool c0 = excl < need && excl + g0 >= need;
+    const bool c1 = excl + g0 < need && excl + g0 + g1 >= need;
+    const int cl = __builtin_ctzll(ballot(c0 | c1) | (1ull << 63));
+    const bool second = readlane(c1 ? 1 : 0, cl) != 0;
+    Crossing r;
+    r.bin = 2 * (64 * cw + cl) + (second ? 1 : 0);
+    r.above = readlane(second ? excl + g0 : excl, cl);
+    r.cnt = readlane(second ? g1 : g0, cl);
+    return r;
 }
 
 // Value buckets: bucket 0 holds the largest values.  A finite value goes to
@@ -671,10 +705,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     }
     if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
     __syncthreads();
-    find_crossing(sh, k);
-    const int bstar = sh.cross_bin;
-    int need = k - sh.cross_above;
-    int cnt = sh.cross_cnt;
+    const Crossing cr = find_crossing_w(sh, k);
+    const int bstar = cr.bin;
+    int need = k - cr.above;
+    int cnt = cr.cnt;
     if (cnt > kCand) {
         __syncthreads();
         return false;
@@ -722,7 +756,25 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
 
     // ---- the k-th pair (T, Ct) -------------------------------------------
     uint32_t T;
-    if (nc <= 64) {
+    if (nc <= kRankAll) {
+        // every wave ranks the few members itself: no barrier
+        const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
+        const int mc = l < nc ? sh.cand_col[l] : 0x7FFFFFFF;
+        int rank = 0;
+        for (int j = 0; j < nc; ++j) {
+            const uint32_t kj = (uint32_t)readlane((int)mk, j);
+            const int cj = readlane(mc, j);
+            rank += (kj > mk || (kj == mk && cj < mc)) ? 1 : 0;
+        }
+        const int kl = __builtin_ctzll(ballot(l < nc && rank == need - 1) | (1ull << 63));
+        T = (uint32_t)readlane((int)mk, kl);
+        const int tc = readlane(mc, kl);
+        // a key equal to the k-th at a later column would be dropped
+        if (ballot(l < nc && mk == T && mc > tc) != 0ull) {
+            __syncthreads();
+            return false;
+        }
+    } else if (nc <= 64) {
         if (w == 0) {
             const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
             const int mc = l < nc ? sh.cand_col[l] : 0x7FFFFFFF;
@@ -768,8 +820,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     for (int j = 0; j < kStageGroups; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sel |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << (4 * j + e);
-    static_assert(kStageGroups * kThreads <= (int)sizeof(int) * kCand, "a byte per group fits cand_col");
-    uint8_t *flags = reinterpret_cast<uint8_t *>(sh.cand_col);  // the members are no longer needed
+    static_assert(kStageGroups * kThreads <= (int)sizeof(uint32_t) * kBins, "a byte per group fits the histogram");
+    // (in the histogram's words: waves still ranking members may read cand_col;
+    // the next row's range clears the histogram)
+    uint8_t *flags = reinterpret_cast<uint8_t *>(sh.hist);
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) flags[t + kThreads * j] = (uint8_t)((sel >> (4 * j)) & 0xFu);
     __syncthreads();
