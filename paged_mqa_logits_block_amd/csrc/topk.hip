@@ -73,6 +73,7 @@ struct Shared {
     int tie_col;
     uint32_t thr_key;
     int ties_cut;  // some keys equal to the k-th are dropped (the column order decides)
+    int ntie;      // fused selection: the tie group's count
     // split selection (resolve kernel)
     int split_above;   // columns of the row above the window
     int split_before;  // columns kept before this slice, known before the resolve
@@ -1551,6 +1552,7 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
     if (t == 0) {
         sh.ncand = 0;
         sh.split_over = 0;
+        sh.ntie = 0;
     }
     const RowRange rr = row_range(sh, kmax, kmin, nf, t);  // clears the histogram; barrier
     int total = 0;
@@ -1579,10 +1581,10 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
         }
     }
     __syncthreads();
-    find_crossing(sh, k);
-    const int bstar = sh.cross_bin;
-    int need = k - sh.cross_above;
-    int cnt = sh.cross_cnt;
+    const Crossing cr = find_crossing_w(sh, k);
+    const int bstar = cr.bin;
+    int need = k - cr.above;
+    int cnt = cr.cnt;
     if (cnt > kCand) return false;
     if (wave_has) {
 #pragma unroll
@@ -1601,7 +1603,12 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
     __syncthreads();
     uint32_t P;
     const int nc = sh.ncand;  // == cnt
-    if (nc <= 64) {  // keys are distinct: rank by key alone
+    if (nc <= kRankAll) {  // keys are distinct: rank by key alone, every wave for itself
+        const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
+        int rank = 0;
+        for (int j = 0; j < nc; ++j) rank += ((uint32_t)readlane((int)mk, j) > mk) ? 1 : 0;
+        P = (uint32_t)readlane((int)mk, __builtin_ctzll(ballot(l < nc && rank == need - 1) | (1ull << 63)));
+    } else if (nc <= 64) {
         if (w == 0) {
             const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
             int rank = 0;
@@ -1615,9 +1622,6 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
             for (int j = t; j < nc; j += kThreads) f(sh.cand_key[j]);
         }, P, need, cnt);
     }
-    __syncthreads();
-    if (t == 0) sh.ncand = 0;  // the tie group's count next
-    __syncthreads();
 
     // ---- 3. kept keys, the tie group, lists that might miss columns ---------
     const uint32_t tstar = P >> 6;
@@ -1641,7 +1645,7 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
                     atomicOr(&bits[col >> 5], 1u << (col & 31));
                     ++above;
                 } else {
-                    const int at = atomicAdd(&sh.ncand, 1);
+                    const int at = atomicAdd(&sh.ntie, 1);
                     if (at < kCandTies) sh.cand_col[at] = col;
                 }
             }
@@ -1670,7 +1674,7 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
     int nabove = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) nabove += sh.grp[i];
-    const int nt = sh.ncand;
+    const int nt = sh.ntie;
     const int need_t = k - nabove;
     if (sh.split_over || nt > kCandTies || need_t < 1 || need_t > nt) return false;
     if (w == 0) {
