@@ -976,7 +976,8 @@ def _fused_vs_two_calls(inp, label, workspace="auto"):
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_verify", "decode_verify_fp16", "decode_verify_d64",
-                                  "single_row_mixed", "fp8_paged"])
+                                  "single_row_mixed", "fp8_paged", "fp8_paged_ragged", "fp8_paged_kvb1",
+                                  "fp8_paged_shuffled"])
 def test_fused_selection_workloads(name):
     inp = qsa_inputs.make_config(name)
     say("fused", name)
@@ -986,6 +987,29 @@ def test_fused_selection_workloads(name):
     tols = assert_logits_match(g.cpu().numpy(), o, inp, label=f"fused {name}")
     oi = oracle.topk(o.astype(np.float32), inp.ctx_lens, inp.topk)
     assert_topk_banded(i.cpu().numpy(), oi, o, tols, label=f"fused {name}")
+
+
+@pytest.mark.parametrize("H,layout,B", [(64, "copacked", 64), (32, "paged", 128), (64, "copacked_shuffled", 64),
+                                        (64, "copacked", 3), (32, "paged", 1)])
+@pytest.mark.parametrize("req_rows", [(4, 4, 4, 4), (7, 8, 1, 3, 2)])
+def test_fused_selection_four_row_fp8(H, layout, B, req_rows):
+    """The full call (qsa_paged_logits_topk) on the 4-row fp8 scorer's shapes,
+    where scoring and selection run unfused inside the one call: 4-row and
+    ragged requests (tiles that follow the requests), block-flat, paged,
+    preshuffled and gathered keys, a row that fits in k; against the two calls
+    bit for bit."""
+    n = sum(req_rows)
+    rng = np.random.default_rng(1200 + H + B + n)
+    ctx = []
+    for nn in req_rows:
+        kv_len = int(rng.choice([1500, 2100, 5000, 9000, 12288]))
+        ctx += [kv_len - nn + j + 1 for j in range(nn)]
+    ctx[0] = 700  # a row that fits in k
+    inp = qsa_inputs.build(name="fused mtp", seed=1300 + H + B + n, req_rows=list(req_rows), ctx_rows=ctx,
+                           num_heads=H, block_size=B, dtype="fp8", layout=layout, weights=True,
+                           width=12288, topk=1024, poison=True)
+    say("fused 4-row fp8", H, layout, B, req_rows)
+    _fused_vs_two_calls(inp, f"fused mtp H{H} {layout} B{B}")
 
 
 @pytest.mark.parametrize("H", [1, 2, 4])
