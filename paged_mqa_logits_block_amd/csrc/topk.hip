@@ -499,9 +499,10 @@ struct RowRange {
     bool all_finite;
 };
 
+// Each wave's finite min / max (as order keys) and non-finite flag, reduced
+// across the wave and written to LDS for range_read.
 template <class Sh>
-__device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite,
-                                              int t = (int)threadIdx.x) {
+__device__ __forceinline__ void range_publish(Sh &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite, int t) {
     const int w = t >> 6;
     kmax = wave_total_umax(kmax);
     const uint32_t nkmin = wave_total_umax(~kmin);
@@ -511,8 +512,11 @@ __device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t km
         sh.red_min[w] = nkmin;
         sh.red_nf[w] = nonfinite;
     }
-    clear_hist(sh);
-    __syncthreads();
+}
+
+// The block's range from the waves' published partials (after a barrier).
+template <class Sh>
+__device__ __forceinline__ RowRange range_read(Sh &sh) {
     uint32_t a = 0, b = 0, c = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) {
@@ -530,6 +534,15 @@ __device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t km
     const bool usable = a != 0u && span > 0.0f && __builtin_isfinite(span) && __builtin_isfinite(scale) &&
                         __builtin_isfinite(vmax * scale);
     return RowRange{vmax, usable ? scale : 0.0f, c == 0u};
+}
+
+template <class Sh>
+__device__ __forceinline__ RowRange row_range(Sh &sh, uint32_t kmax, uint32_t kmin, uint32_t nonfinite,
+                                              int t = (int)threadIdx.x) {
+    range_publish(sh, kmax, kmin, nonfinite, t);
+    clear_hist(sh);
+    __syncthreads();
+    return range_read(sh);
 }
 
 // running finite range and non-finite flag over one visible value
@@ -655,7 +668,19 @@ __device__ __forceinline__ int fast_bucket(float v, float s, float off) {
     return 1 + max(min((int)__builtin_fmaf(v, -s, off), kBins - 3), 0);
 }
 
-__device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups], int n, int k, int32_t *out) {
+// The bucket map of the workgroup's previous row (its own range, handed on
+// when it completed this path): the next row's histogram is taken with it in
+// the same pass as that row's range, which saves the range's barrier.  The map
+// is monotone whatever row it came from, and the end buckets are open-ended,
+// so the crossing and its members stay exact; only a crossing bucket too
+// crowded for the member list sends the row to a histogram over its own range.
+struct FastMap {
+    float sc, off;
+    bool valid;
+};
+
+__device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups], int n, int k, int32_t *out,
+                                            FastMap &map) {
     int t = threadIdx.x;
     // opaque to the optimiser: column indices derived from t are recomputed
     // per row rather than kept live (in registers the row needs) across rows
@@ -671,6 +696,23 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     // first thread of this wave, as a scalar: whether a wave's group j reaches
     // past n is uniform, so waves whose columns are all visible skip the fixes
     const int wt0 = __builtin_amdgcn_readfirstlane(t & ~63);
+    const FastMap pm = map;
+    map.valid = false;
+    // the histogram of the row's visible columns over a map (counts of the
+    // last group's columns past n are 0)
+    auto histogram = [&](float hs, float hoff) {
+#pragma unroll
+        for (int j = 0; j < kStageGroups; ++j) {
+            const int i = t + kThreads * j;
+            if (4 * i + 4 <= n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], hs, hoff)], 1u);
+            } else if (i < n4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], hs, hoff)], e < tail ? 1u : 0u);
+            }
+        }
+    };
     float mx = x[0][0], mn = x[0][0];
 #pragma unroll
     for (int j = 0; j < kStageGroups; ++j) {
@@ -685,28 +727,43 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
         mn = __builtin_elementwise_minimum(mn, __builtin_elementwise_minimum(x[j][2], x[j][3]));
     }
     const bool fin = __builtin_isfinite(mx) && __builtin_isfinite(mn);
-    const RowRange rr = row_range(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
-    if (!rr.all_finite) {
+    float sc = pm.sc, off = pm.off;
+    RowRange rr;
+    Crossing cr;
+    if (pm.valid) {
+        // the previous row's map, before the range's barrier (the histogram
+        // was left cleared); a non-finite value's bucket is clamped, and the
+        // row then leaves this path
+        histogram(sc, off);
+        range_publish(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
+        if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
         __syncthreads();
-        return false;
-    }
-    const float sc = rr.scale, off = rr.vmax * rr.scale;
-
-    // ---- histogram (cleared by row_range) --------------------------------
-#pragma unroll
-    for (int j = 0; j < kStageGroups; ++j) {
-        const int i = t + kThreads * j;
-        if (4 * i + 4 <= n) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], sc, off)], 1u);
-        } else if (i < n4) {  // the last group: columns past n add 0
-#pragma unroll
-            for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[fast_bucket(x[j][e], sc, off)], e < tail ? 1u : 0u);
+        rr = range_read(sh);
+        if (!rr.all_finite) {
+            __syncthreads();
+            return false;
         }
+        cr = find_crossing_w(sh, k);
     }
-    if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
-    __syncthreads();
-    const Crossing cr = find_crossing_w(sh, k);
+    if (!pm.valid || cr.cnt > kCand) {  // the row's own map
+        if (pm.valid) {
+            __syncthreads();  // every wave is done reading the histogram
+            clear_hist(sh);
+            __syncthreads();
+        } else {
+            rr = row_range(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
+            if (!rr.all_finite) {
+                __syncthreads();
+                return false;
+            }
+        }
+        sc = rr.scale;
+        off = rr.vmax * rr.scale;
+        histogram(sc, off);
+        if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
+        __syncthreads();
+        cr = find_crossing_w(sh, k);
+    }
     const int bstar = cr.bin;
     int need = k - cr.above;
     int cnt = cr.cnt;
@@ -847,6 +904,12 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             ++p;
         }
     }
+    // this row's own map for the next row, with the histogram (the kept flags,
+    // read above) cleared for it
+    map.sc = rr.scale;
+    map.off = rr.vmax * rr.scale;
+    map.valid = rr.scale > 0.0f;
+    clear_hist(sh);
     __syncthreads();
     // the k columns stay in sh.cand_key; the caller writes them to `out`
     // (flush_kept) when their stores cannot hold up a wait on its prefetch
@@ -932,6 +995,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
     if (fast_row(n, st)) prefetch(row, n, st);
     f32x4 x[kStageGroups];
     int32_t *pend = nullptr;  // the previous row's output, its columns still in LDS
+    FastMap fmap{0.0f, 0.0f, false};  // the register path's map for its next row
 #pragma unroll 1
     for (int m = 0;; ++m) {
         const int nxt = row + stride;
@@ -959,7 +1023,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         int32_t *out = a.idx_out + (int64_t)row * k;
         if (n <= k) {
             for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
-        } else if (fast && select_fast(sh, x, n, k, out)) {
+        } else if (fast && select_fast(sh, x, n, k, out, fmap)) {
             pend = out;
         } else {
             if (t == 0) later[m >> 5] |= 1u << (m & 31);
