@@ -611,6 +611,33 @@ def test_topk_many_rows_infinities_and_fallbacks(rows):
     assert_topk_exact(g, oracle.topk(x, ctx, k), label=f"many rows inf {rows}")
 
 
+def test_topk_rows_map_from_previous_row():
+    """One workgroup per row, rows r, r + 256, r + 512 in one workgroup: each row's
+    histogram is first taken on the previous row's bucket map.  Rows shifted far
+    above the previous row's range (every value in the top bucket), far below it
+    (every value in the bottom bucket), much narrower inside it, and with an
+    infinity after a finite row: the crossing stays exact, or the row
+    falls back to its own map or the set-aside path; every row equals the oracle."""
+    W, k, R = 9000, 2048, 1280
+    rng = np.random.default_rng(4242)
+    ctx = rng.integers(k + 1, W + 1, size=R)
+    base = qsa_inputs.make_logits(R, W, ctx, seed=4243, kind="normal")
+    x = base.copy()
+    blk = np.arange(R) // 256
+    vis = np.arange(W)[None, :] < ctx[:, None]
+    x[blk == 1] = np.where(vis[blk == 1], x[blk == 1] + np.float32(1000.0), x[blk == 1])  # above
+    x[blk == 2] = np.where(vis[blk == 2], x[blk == 2] - np.float32(5000.0), x[blk == 2])  # below
+    x[blk == 3] = np.where(vis[blk == 3], x[blk == 3] * np.float32(1e-4), x[blk == 3])    # narrow
+    for r in np.nonzero(blk == 4)[0][::5]:
+        x[r, int(rng.integers(0, ctx[r]))] = np.float32(-np.inf) if r % 2 else np.float32(np.inf)
+    x = x.astype(np.float32)
+    say("topk map from previous row")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    g = gpu_topk(xt, ct, k, workspace=None).cpu().numpy()
+    assert_topk_exact(g, oracle.topk(x, ctx, k), label="map from previous row")
+
+
 def test_topk_sample_miss_falls_back():
     """Rows whose sampled columns are far below (or above) the rest: the
     sample's window misses the k-th value and the row takes the histogram
