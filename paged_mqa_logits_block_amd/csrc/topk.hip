@@ -74,6 +74,11 @@ struct Shared {
     uint32_t thr_key;
     int ties_cut;  // some keys equal to the k-th are dropped (the column order decides)
     int ntie;      // fused selection: the tie group's count
+    // register path: the previous row's kept columns (n <= kStage < 65536),
+    // written out after the next row's first barrier, and the kept counts of
+    // each (group slice, wave)
+    uint16_t kept16[kCand];
+    alignas(16) uint32_t ktot[kStageGroups * kWaves];
     // split selection (resolve kernel)
     int split_above;   // columns of the row above the window
     int split_before;  // columns kept before this slice, known before the resolve
@@ -679,8 +684,14 @@ struct FastMap {
     bool valid;
 };
 
+// Writes the k column indices of the workgroup's previous register-path row
+// (left in sh.kept16) to `out`.
+__device__ __forceinline__ void flush_kept(const Shared &sh, int k, int32_t *out) {
+    for (int p = threadIdx.x; p < k; p += kThreads) out[p] = (int32_t)sh.kept16[p];
+}
+
 __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups], int n, int k, int32_t *out,
-                                            FastMap &map) {
+                                            int32_t *&pend, FastMap &map) {
     int t = threadIdx.x;
     // opaque to the optimiser: column indices derived from t are recomputed
     // per row rather than kept live (in registers the row needs) across rows
@@ -738,6 +749,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
         range_publish(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
         if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
         __syncthreads();
+        if (pend) {  // the previous row's kept list (ordered by the barrier)
+            flush_kept(sh, k, pend);
+            pend = nullptr;
+        }
         rr = range_read(sh);
         if (!rr.all_finite) {
             __syncthreads();
@@ -752,6 +767,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             __syncthreads();
         } else {
             rr = row_range(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
+            if (pend) {
+                flush_kept(sh, k, pend);
+                pend = nullptr;
+            }
             if (!rr.all_finite) {
                 __syncthreads();
                 return false;
@@ -868,58 +887,72 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     }
     const float Tf = key_value(T);
 
-    // ---- the kept set in column order, through LDS -----------------------
-    // Each float4 group's kept flags go to LDS as one byte (group i: byte i,
-    // columns 4i .. 4i+3 in its low 4 bits); thread t then ranks columns
-    // 32t .. 32t+31 from two words of that byte array: popcounts, a wave scan
-    // and one scan of the wave totals give its first place in the kept list.
-    uint32_t sel = 0u;
-#pragma unroll
-    for (int j = 0; j < kStageGroups; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sel |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << (4 * j + e);
+    // ---- the kept set in column order -----------------------------------
+    // Slice j of wave w (its lanes' group j) is the 256 columns from
+    // 4096 j + 256 w, so the column order of the slices is (j, w).  The wave
+    // turns its 8 x 64 flag nibbles around through its own 512 bytes of the
+    // histogram's words (last read before the members' barrier; no other wave
+    // touches them): lane l then holds the 32 consecutive columns from
+    // 4096 (l / 8) + 256 w + 32 (l % 8) as one flag byte per float4 group.  A
+    // scan over each 8-lane segment ranks them inside the slice, and one scan
+    // of the 128 slice totals in (j, w) order, after one barrier, places the
+    // slices.  Each wave then clears its part of the histogram for the next row.
+    uint8_t *wf = reinterpret_cast<uint8_t *>(sh.hist) + 512 * w;
     static_assert(kStageGroups * kThreads <= (int)sizeof(uint32_t) * kBins, "a byte per group fits the histogram");
-    // (in the histogram's words: waves still ranking members may read cand_col;
-    // the next row's range clears the histogram)
-    uint8_t *flags = reinterpret_cast<uint8_t *>(sh.hist);
 #pragma unroll
-    for (int j = 0; j < kStageGroups; ++j) flags[t + kThreads * j] = (uint8_t)((sel >> (4 * j)) & 0xFu);
-    __syncthreads();
-    const uint2 fw = reinterpret_cast<const uint2 *>(flags)[t];  // groups 8t .. 8t+7
+    for (int j = 0; j < kStageGroups; ++j) {
+        uint32_t nib = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nib |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << e;
+        wf[64 * j + l] = (uint8_t)nib;
+    }
+    const uint2 fw = reinterpret_cast<const uint2 *>(wf)[l];  // lanes 8 (l % 8) .. +7 of slice l / 8
+    {
+        uint32_t z;  // made here: a zero pair kept live across the row loop was spilled
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        reinterpret_cast<uint2 *>(wf)[l] = make_uint2(z, z);
+    }
     const int mine = __popc(fw.x) + __popc(fw.y);
-    const int incl = wave_incl_sum(mine);
-    if (l == 63) sh.wave_tot[w] = incl;
+    int seg = mine;  // inclusive scan over the lane's 8-lane segment
+    {
+        const int s1 = __builtin_amdgcn_update_dpp(0, seg, kDppRowShr1, 0xF, 0xF, false);
+        seg += (l & 7) >= 1 ? s1 : 0;
+        const int s2 = __builtin_amdgcn_update_dpp(0, seg, kDppRowShr2, 0xF, 0xF, false);
+        seg += (l & 7) >= 2 ? s2 : 0;
+        const int s4 = __builtin_amdgcn_update_dpp(0, seg, kDppRowShr4, 0xF, 0xF, false);
+        seg += (l & 7) >= 4 ? s4 : 0;
+    }
+    if ((l & 7) == 7) sh.ktot[kWaves * (l >> 3) + w] = (uint32_t)seg;
     __syncthreads();
-    const int wt = l < kWaves ? sh.wave_tot[l] : 0;
-    const int wincl = wave_incl_sum(wt);
-    int p = readlane(wincl - wt, w) + incl - mine;
-    uint32_t *kept = sh.cand_key;  // k <= kCand column indices, in order
+    int p;
+    {
+        const uint2 tt2 = reinterpret_cast<const uint2 *>(sh.ktot)[l];  // slices 2l, 2l + 1 in (j, w) order
+        const int a0 = (int)tt2.x, a1 = (int)tt2.y;
+        const int incl = wave_incl_sum(a0 + a1);
+        const int before = (w & 1) ? incl - a1 : incl - a0 - a1;  // kept before slice 2l + (w & 1)
+        p = shfl_i(before, (kWaves * (l >> 3) + w) >> 1) + seg - mine;
+    }
+    uint16_t *kept = sh.kept16;
+    const int c0 = 4096 * (l >> 3) + 256 * w + 32 * (l & 7);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        uint32_t word = h ? fw.y : fw.x;  // bit 8b + e: column 32t + 16h + 4b + e
+        uint32_t word = h ? fw.y : fw.x;  // bit 8b + e: column c0 + 16h + 4b + e
         while (word) {
             const int b = __builtin_ctz(word);
             word &= word - 1u;
-            if (p < k) kept[p] = (uint32_t)(32 * t + 16 * h + 4 * (b >> 3) + (b & 7));
+            if (p < k) kept[p] = (uint16_t)(c0 + 16 * h + 4 * (b >> 3) + (b & 7));
             ++p;
         }
     }
-    // this row's own map for the next row, with the histogram (the kept flags,
-    // read above) cleared for it
+    // this row's own map for the next row
     map.sc = rr.scale;
     map.off = rr.vmax * rr.scale;
     map.valid = rr.scale > 0.0f;
-    clear_hist(sh);
-    __syncthreads();
-    // the k columns stay in sh.cand_key; the caller writes them to `out`
-    // (flush_kept) when their stores cannot hold up a wait on its prefetch
-    (void)out;
+    // the k columns stay in sh.kept16 until the next row's first barrier (or
+    // the caller's), when their stores no longer hold up a wait on the
+    // caller's prefetch
+    pend = out;
     return true;
-}
-
-// Writes the k column indices select_fast left in sh.cand_key.
-__device__ __forceinline__ void flush_kept(const Shared &sh, int k, int32_t *out) {
-    for (int p = threadIdx.x; p < k; p += kThreads) out[p] = (int32_t)sh.cand_key[p];
 }
 
 // Rows of a many-row call, round robin over a grid of workgroups that each take
@@ -1006,7 +1039,6 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         // Every thread reads back only the slots its own lane copied, so the
         // copy needs no barrier: the wave's wait covers its own copies, and the
         // reads complete before the next copy into the same slots is issued.
-        // The kept columns were ordered by select_fast's last barrier.
         if (fast) {
             wait_dma();
             int tt = t;
@@ -1014,17 +1046,19 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
 #pragma unroll
             for (int j = 0; j < kStageGroups; ++j) x[j] = pref[tt + kThreads * j];
         }
-        if (pend) {
-            flush_kept(sh, k, pend);
-            pend = nullptr;
-        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (more && fast_row(nn, nst)) prefetch(nxt, nn, nst);
         int32_t *out = a.idx_out + (int64_t)row * k;
+        // The previous row's kept list is written out after the first barrier
+        // of select_fast, or here for a row that does not take it.
+        if (pend && !fast) {
+            __syncthreads();
+            flush_kept(sh, k, pend);
+            pend = nullptr;
+        }
         if (n <= k) {
             for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
-        } else if (fast && select_fast(sh, x, n, k, out, fmap)) {
-            pend = out;
+        } else if (fast && select_fast(sh, x, n, k, out, pend, fmap)) {
         } else {
             if (t == 0) later[m >> 5] |= 1u << (m & 31);
             any_later = true;
@@ -1035,7 +1069,10 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         n = nn;
         st = nst;
     }
-    if (pend) flush_kept(sh, k, pend);
+    if (pend) {
+        __syncthreads();
+        flush_kept(sh, k, pend);
+    }
     if (!any_later) return;
     __syncthreads();
 #pragma unroll 1
