@@ -14,11 +14,15 @@ namespace {
 // walks its column range 32 columns (one 8 KB run of keys inside one pool
 // block) per step.  The producer fetches runs D steps ahead into a ring of its
 // own registers with contiguous 16-byte loads -- the fetch competes with the
-// output stream for HBM and its latency is long -- and writes each run to LDS
-// one step ahead of use, every key padded to 272 bytes so that the consumers
-// read their MFMA fragments without bank conflicts.  (Fragment loads straight
-// from global memory would touch a different cache line in every lane.)  LDS
-// holds two runs, one barrier per step.  The consumers issue no global loads
+// output stream for HBM and its latency is long -- and writes them to LDS one
+// phase of 8 steps ahead of use, every key padded to 272 bytes so that the
+// consumers read their MFMA fragments without bank conflicts.  (Fragment loads
+// straight from global memory would touch a different cache line in every
+// lane.)  LDS holds two phases of runs, with one barrier per phase: between
+// barriers the consumer waves drift apart, so that one wave's LDS reads and
+// stores overlap another's MFMAs instead of every wave waiting on the same
+// pipe at once (one barrier per step was 11% slower, one per 4 steps 1.5%).
+// The consumers issue no global loads
 // in the loop, so their stores never wait behind a key fetch (loads and
 // stores share one counter on gfx9).  Steps past the workgroup's visible
 // range only store -inf.
@@ -53,6 +57,7 @@ typedef uint32_t pf_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPfKeyLds = 272;               // padded key in LDS (bytes)
 constexpr int kPfRunLds = 32 * kPfKeyLds;    // one 32-key run
 constexpr int kPfDepth = 4;                  // runs in flight per workgroup
+constexpr int kPfPhase = 8;                  // steps between barriers (LDS holds two phases of runs)
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data)
 constexpr int kDropOffset = (int)0x80000000u;  // beyond any descriptor range used here
 
@@ -61,8 +66,10 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
     constexpr int H = 4;
     constexpr int D = kPfDepth;
     constexpr int LPL = 8192 / (16 * 64);  // 16-byte loads per producer lane per run
-    __shared__ __align__(16) uint8_t kbuf[2][kPfRunLds];
-    __shared__ int okbuf[2];
+    constexpr int S = kPfPhase;
+    static_assert(S % D == 0, "a phase is whole rounds of the ring");
+    __shared__ __align__(16) uint8_t kbuf[2 * S][kPfRunLds];
+    __shared__ int okbuf[2 * S];
     __shared__ __align__(16) float wsm[HAS_W ? NW : 1][16][4];  // weights of each consumer's rows
 
     const int l = lane_id();
@@ -80,7 +87,7 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
     }
     vis_wg = readlane(wave_max_i(vis_wg), 0);
     const int nA = vis_wg > c0 ? min(nsteps, (vis_wg - c0 + 31) / 32) : 0;  // scored steps
-    const int nR = (nA + D - 1) / D * D;  // steps of the loop (whole rounds of D)
+    const int nR = (nA + kPfPhase - 1) / kPfPhase * kPfPhase;  // steps of the loop (whole phases)
 
     if (w == NW) {  // producer
         if (nA == 0) return;
@@ -123,18 +130,30 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
         bool okr[D];
 #pragma unroll
         for (int k = 0; k < D; ++k) okr[k] = fetch(ring[k]);  // runs 0 .. D-1
-        put(0, ring[0], okr[0]);
-        __syncthreads();
-        // step st (slot k = st mod D): fetch run st + D into slot k (run st
-        // left it one step ago), run st + 1 to LDS, barrier
+        // each run put to LDS makes room in the ring for the run D later
 #pragma unroll 1
-        for (int st = 0; st < nR; st += D) {
+        for (int kk = 0; kk < S; kk += D) {
 #pragma unroll
             for (int k = 0; k < D; ++k) {
+                put(kk + k, ring[k], okr[k]);  // runs 0 .. S-1 to the first half
                 okr[k] = fetch(ring[k]);
-                put((k + 1) & 1, ring[(k + 1) % D], okr[(k + 1) % D]);
-                __syncthreads();
             }
+        }
+        __syncthreads();
+        // phase ph (runs S ph .. S ph + S-1 being scored from LDS half ph & 1):
+        // the next phase's runs to the other half, barrier
+#pragma unroll 1
+        for (int st = 0; st < nR; st += S) {
+            const int half = ((st / S) + 1) & 1;
+#pragma unroll 1
+            for (int kk = 0; kk < S; kk += D) {
+#pragma unroll
+                for (int k = 0; k < D; ++k) {
+                    put(S * half + kk + k, ring[k], okr[k]);
+                    okr[k] = fetch(ring[k]);
+                }
+            }
+            __syncthreads();
         }
         return;
     }
@@ -211,7 +230,11 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
             float v = 0.0f;
             if (HAS_W) {
                 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-                const f32x4_t wq = *reinterpret_cast<const f32x4_t *>(&wsm[w][8 * mt + 2 * q + gk][0]);
+                // an opaque zero keeps these reads in the loop: hoisted out of
+                // it, the weights take 32 registers and the loop spills
+                int z = 0;
+                asm volatile("" : "+v"(z));
+                const f32x4_t wq = *reinterpret_cast<const f32x4_t *>(&wsm[w][8 * mt + 2 * q + gk + z][0]);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) v += wq[h] * relu(acc[4 * q + h]);
             } else {
@@ -225,22 +248,24 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
     };
 
     if (nA > 0) {
-        __syncthreads();  // run 0 in kbuf[0]
+        __syncthreads();  // runs 0 .. S-1 in the first half
         // Step st, two stages per M tile: MFMAs of tile 0 for run st beside
         // the epilogue of tile 1 for run st - 1, then MFMAs of tile 1 beside
-        // the epilogue of tile 0 for run st; barrier.  The epilogue of tile 1
-        // for the last run follows the loop (step -1's is dropped).
+        // the epilogue of tile 0 for run st; a barrier after every S steps.
+        // The epilogue of tile 1 for the last run follows the loop (step -1's
+        // is dropped).
         f32x16 acc0, acc1 = f32x16{};
         bool ok_prev = false;
 #pragma unroll 1
-        for (int st = 0; st < nR; st += 2) {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint8_t *kf = kbuf[k] + (l & 31) * kPfKeyLds + 16 * gk;
+        for (int st = 0; st < nR; st += S) {
+            const int half = (st / S) & 1;
+#pragma unroll 1
+            for (int k = 0; k < S; ++k) {
+                const uint8_t *kf = kbuf[S * half + k] + (l & 31) * kPfKeyLds + 16 * gk;
                 pf_v8 b[8];
 #pragma unroll
                 for (int s2 = 0; s2 < 8; ++s2) b[s2] = *reinterpret_cast<const pf_v8 *>(kf + 32 * s2);
-                const bool ok = __builtin_amdgcn_readfirstlane(okbuf[k]) != 0;
+                const bool ok = __builtin_amdgcn_readfirstlane(okbuf[S * half + k]) != 0;
                 acc0 = f32x16{};
 #pragma unroll
                 for (int s2 = 0; s2 < 8; ++s2)
@@ -252,8 +277,8 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
                     acc1 = P::mma(qa[1][s2], b[s2], acc1);
                 epilogue(0, st + k, acc0, ok);
                 ok_prev = ok;
-                __syncthreads();
             }
+            __syncthreads();
         }
         epilogue(1, nR - 1, acc1, ok_prev);
     }
