@@ -57,6 +57,7 @@ typedef uint32_t pf_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPfKeyLds = 272;               // padded key in LDS (bytes)
 constexpr int kPfRunLds = 32 * kPfKeyLds;    // one 32-key run
 constexpr int kPfDepth = 4;                  // runs in flight per workgroup
+constexpr int kPfEarly = 4;                  // next-step key fragments read before the epilogue
 constexpr int kPfPhase = 8;                  // steps between barriers (LDS holds two phases of runs)
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data)
 constexpr int kDropOffset = (int)0x80000000u;  // beyond any descriptor range used here
@@ -254,17 +255,24 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
         // the epilogue of tile 0 for run st; a barrier after every S steps.
         // The epilogue of tile 1 for the last run follows the loop (step -1's
         // is dropped).
+        // The next step's key fragments are read into b as tile 1's MFMAs
+        // release it (the first kPfEarly before tile 0's epilogue, the rest
+        // after it, within the register budget), so their LDS latency passes
+        // under the rest of the step (the last step of a phase re-reads its
+        // own run: the next phase's first run is read after the barrier).
         f32x16 acc0, acc1 = f32x16{};
         bool ok_prev = false;
+        const int lane_off = (l & 31) * kPfKeyLds + 16 * gk;
 #pragma unroll 1
         for (int st = 0; st < nR; st += S) {
             const int half = (st / S) & 1;
+            pf_v8 b[8];
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                b[s2] = *reinterpret_cast<const pf_v8 *>(kbuf[S * half] + lane_off + 32 * s2);
 #pragma unroll 1
             for (int k = 0; k < S; ++k) {
-                const uint8_t *kf = kbuf[S * half + k] + (l & 31) * kPfKeyLds + 16 * gk;
-                pf_v8 b[8];
-#pragma unroll
-                for (int s2 = 0; s2 < 8; ++s2) b[s2] = *reinterpret_cast<const pf_v8 *>(kf + 32 * s2);
+                const uint8_t *kn = kbuf[S * half + min(k + 1, S - 1)] + lane_off;
                 const bool ok = __builtin_amdgcn_readfirstlane(okbuf[S * half + k]) != 0;
                 acc0 = f32x16{};
 #pragma unroll
@@ -273,9 +281,13 @@ __global__ __launch_bounds__(64 * (NW + 1), 3) void prefill_logits_kernel(Logits
                 epilogue(1, st + k - 1, acc1, ok_prev);
                 acc1 = f32x16{};
 #pragma unroll
-                for (int s2 = 0; s2 < 8; ++s2)
+                for (int s2 = 0; s2 < 8; ++s2) {
                     acc1 = P::mma(qa[1][s2], b[s2], acc1);
+                    if (s2 < kPfEarly) b[s2] = *reinterpret_cast<const pf_v8 *>(kn + 32 * s2);
+                }
                 epilogue(0, st + k, acc0, ok);
+#pragma unroll
+                for (int s2 = kPfEarly; s2 < 8; ++s2) b[s2] = *reinterpret_cast<const pf_v8 *>(kn + 32 * s2);
                 ok_prev = ok;
             }
             __syncthreads();
