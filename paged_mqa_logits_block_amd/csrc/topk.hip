@@ -51,7 +51,7 @@ constexpr int kBins = 2048;
 constexpr int kStage = 32768;    // longest row staged in LDS
 constexpr int kMaxWidth = 69632;
 constexpr int kCand = 2048;      // (key, column) list of the crossing bucket
-constexpr int kRankAll = 24;     // member lists this short are ranked by every wave
+constexpr int kRankAll = 24;     // fused resolve: member lists this short are ranked by every wave
 constexpr int kChunk = 8;        // float4 groups ranked per compaction round
 constexpr int kStageGroups = kStage / 4 / kThreads;
 constexpr int kMaxGroups = (kMaxWidth + 4 * kThreads - 1) / (4 * kThreads);
@@ -832,26 +832,11 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     }
 
     // ---- the k-th pair (T, Ct) -------------------------------------------
+    // (one wave ranks a short list and hands the result on through LDS: 16
+    // waves ranking it each for itself, without the barrier, were slower once
+    // the kept set needed fewer barriers)
     uint32_t T;
-    if (nc <= kRankAll) {
-        // every wave ranks the few members itself: no barrier
-        const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
-        const int mc = l < nc ? sh.cand_col[l] : 0x7FFFFFFF;
-        int rank = 0;
-        for (int j = 0; j < nc; ++j) {
-            const uint32_t kj = (uint32_t)readlane((int)mk, j);
-            const int cj = readlane(mc, j);
-            rank += (kj > mk || (kj == mk && cj < mc)) ? 1 : 0;
-        }
-        const int kl = __builtin_ctzll(ballot(l < nc && rank == need - 1) | (1ull << 63));
-        T = (uint32_t)readlane((int)mk, kl);
-        const int tc = readlane(mc, kl);
-        // a key equal to the k-th at a later column would be dropped
-        if (ballot(l < nc && mk == T && mc > tc) != 0ull) {
-            __syncthreads();
-            return false;
-        }
-    } else if (nc <= 64) {
+    if (nc <= 64) {
         if (w == 0) {
             const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
             const int mc = l < nc ? sh.cand_col[l] : 0x7FFFFFFF;
