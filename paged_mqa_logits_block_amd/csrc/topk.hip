@@ -522,13 +522,13 @@ __device__ __forceinline__ void range_publish(Sh &sh, uint32_t kmax, uint32_t km
 // The block's range from the waves' published partials (after a barrier).
 template <class Sh>
 __device__ __forceinline__ RowRange range_read(Sh &sh) {
-    uint32_t a = 0, b = 0, c = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        a = max(a, sh.red_max[i]);
-        b = max(b, sh.red_min[i]);
-        c = max(c, sh.red_nf[i]);
-    }
+    // lane i < kWaves takes wave i's partials (all lanes active); the lane
+    // index is made here: one kept live across the row loop was spilled
+    int li;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(li));
+    const uint32_t a = wave_total_umax(li < kWaves ? sh.red_max[li] : 0u);
+    const uint32_t b = wave_total_umax(li < kWaves ? sh.red_min[li] : 0u);
+    const uint32_t c = wave_total_umax(li < kWaves ? sh.red_nf[li] : 0u);
     // with no finite value at all, a = 0 and ~b = ~0: the map is never used
     const float vmax = key_value(a), vmin = key_value(~b);
     const float span = vmax - vmin;
