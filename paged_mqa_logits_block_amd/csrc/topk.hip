@@ -690,8 +690,12 @@ __device__ __forceinline__ void flush_kept(const Shared &sh, int k, int32_t *out
     for (int p = threadIdx.x; p < k; p += kThreads) out[p] = (int32_t)sh.kept16[p];
 }
 
+// `issue` is called once, by every thread, just before the row's first
+// barrier: the caller issues its next row's prefetch there, when the waves
+// that finish their histogram early would otherwise wait.
+template <class Issue>
 __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups], int n, int k, int32_t *out,
-                                            int32_t *&pend, FastMap &map) {
+                                            int32_t *&pend, FastMap &map, Issue &&issue) {
     int t = threadIdx.x;
     // opaque to the optimiser: column indices derived from t are recomputed
     // per row rather than kept live (in registers the row needs) across rows
@@ -748,6 +752,7 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
         histogram(sc, off);
         range_publish(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
         if (t == 0) sh.ncand = 0;  // the member count below (its barriers order it)
+        issue();
         __syncthreads();
         if (pend) {  // the previous row's kept list (ordered by the barrier)
             flush_kept(sh, k, pend);
@@ -766,6 +771,7 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             clear_hist(sh);
             __syncthreads();
         } else {
+            issue();
             rr = row_range(sh, fin ? order_key(mx) : 0u, fin ? order_key(mn) : 0xFFFFFFFFu, fin ? 0u : 1u, t);
             if (pend) {
                 flush_kept(sh, k, pend);
@@ -1032,7 +1038,12 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
             for (int j = 0; j < kStageGroups; ++j) x[j] = pref[tt + kThreads * j];
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (more && fast_row(nn, nst)) prefetch(nxt, nn, nst);
+        auto issue_next = [&]() {
+            if (more && fast_row(nn, nst)) prefetch(nxt, nn, nst);
+        };
+        // (a row that takes the register path issues it before its first
+        // barrier; any other row here)
+        if (!fast) issue_next();
         int32_t *out = a.idx_out + (int64_t)row * k;
         // The previous row's kept list is written out after the first barrier
         // of select_fast, or here for a row that does not take it.
@@ -1043,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkArgs a) {
         }
         if (n <= k) {
             for (int j = t; j < k; j += kThreads) out[j] = j < n ? j : -1;
-        } else if (fast && select_fast(sh, x, n, k, out, pend, fmap)) {
+        } else if (fast && select_fast(sh, x, n, k, out, pend, fmap, issue_next)) {
         } else {
             if (t == 0) later[m >> 5] |= 1u << (m & 31);
             any_later = true;
