@@ -954,10 +954,13 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
 // These loads are issued from inline assembly: the compiler then neither
 // knows of them nor orders the selection's own LDS accesses behind them (it
 // would, for the builtin form, wait for every one before any LDS access); the
-// wait for them is explicit.  A row's output indices are stored at the top of
-// the next iteration, before that iteration's prefetch is issued: stores and
-// loads retire in order on one counter, so stores issued after a prefetch would
-// make the next wait on the prefetch also wait out the stores' latency.  Rows the register path does not take (longer than
+// wait for them is explicit.  They are issued just before a row's first
+// barrier, when early waves would wait anyway (issued at the top of the row,
+// all 16 waves queued their copies at once and the last waves stalled).  A
+// row's output indices stay in LDS until the next row's first barrier and are
+// stored then: stores and loads retire in order on one counter, so the next
+// wait on a prefetch also waits for stores issued before it, which by then
+// have long completed.  Rows the register path does not take (longer than
 // kStage, or refused by select_fast) are marked and selected after the loop by
 // the staged or streaming selection.
 constexpr int kRowsPerGroup = 2048;
