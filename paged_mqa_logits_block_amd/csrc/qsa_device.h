@@ -123,10 +123,25 @@ struct OpMaxU {
 // inclusive prefix sum across the (fully active) wave
 __device__ __forceinline__ int wave_incl_sum(int v) { return wave_scan_dpp(v, 0, OpAdd()); }
 
+// The same inside each 16-lane row only (row_shr 1, 2, 4, 8): lanes 0..15 hold
+// the scan of lanes 0..15.  All 64 lanes must be active.
+template <class Op>
+__device__ __forceinline__ int row16_scan_dpp(int v, int identity, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr1, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr2, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr4, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr8, 0xF, 0xF, false));
+    return v;
+}
+
 // wave-uniform sum / unsigned max (result read from the last lane)
 __device__ __forceinline__ int wave_total_sum(int v) { return readlane(wave_incl_sum(v), 63); }
 __device__ __forceinline__ uint32_t wave_total_umax(uint32_t v) {
     return (uint32_t)readlane(wave_scan_dpp((int)v, 0, OpMaxU()), 63);
+}
+// unsigned max of lanes 0..15 (all lanes active)
+__device__ __forceinline__ uint32_t row16_total_umax(uint32_t v) {
+    return (uint32_t)readlane(row16_scan_dpp((int)v, 0, OpMaxU()), 15);
 }
 
 // v + (v of lane l ^ 16) and v + (v of lane l ^ 32), each with one gfx950

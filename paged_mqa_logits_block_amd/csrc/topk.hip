@@ -179,7 +179,7 @@ __device__ __forceinline__ Crossing find_crossing_w(Shared &sh, int need) {
     if (l == 63) sh.wave_tot[w] = incl;
     __syncthreads();
     const int wt = l < kWaves ? sh.wave_tot[l] : 0;
-    const int winc = wave_incl_sum(wt);
+    const int winc = row16_scan_dpp(wt, 0, OpAdd());  // lanes 0..15: the waves' running totals
     const int cw = __builtin_ctzll(ballot(l < kWaves && winc >= need) | (1ull << (kWaves - 1)));
     const int before = readlane(winc - wt, cw);
     const int b = 2 * (64 * cw + l);
@@ -526,9 +526,10 @@ __device__ __forceinline__ RowRange range_read(Sh &sh) {
     // index is made here: one kept live across the row loop was spilled
     int li;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(li));
-    const uint32_t a = wave_total_umax(li < kWaves ? sh.red_max[li] : 0u);
-    const uint32_t b = wave_total_umax(li < kWaves ? sh.red_min[li] : 0u);
-    const uint32_t c = wave_total_umax(li < kWaves ? sh.red_nf[li] : 0u);
+    static_assert(kWaves == 16, "one 16-lane row holds the waves' partials");
+    const uint32_t a = row16_total_umax(li < kWaves ? sh.red_max[li] : 0u);
+    const uint32_t b = row16_total_umax(li < kWaves ? sh.red_min[li] : 0u);
+    const uint32_t c = row16_total_umax(li < kWaves ? sh.red_nf[li] : 0u);
     // with no finite value at all, a = 0 and ~b = ~0: the map is never used
     const float vmax = key_value(a), vmin = key_value(~b);
     const float span = vmax - vmin;
