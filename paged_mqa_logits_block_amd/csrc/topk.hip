@@ -1163,7 +1163,7 @@ __device__ __forceinline__ RangeBucketer make_range(float vmax, float vmin, int 
 // unsigned max over the kWaves per-wave partials (one LDS read per wave)
 __device__ __forceinline__ uint32_t partials_umax(const uint32_t *red) {
     const int l = lane_id();
-    return wave_total_umax(l < kWaves ? red[l] : 0u);
+    return row16_total_umax(l < kWaves ? red[l] : 0u);
 }
 
 // Bin of hist (64 * 4 * Q bins, in order) where the running count first
@@ -1546,7 +1546,7 @@ __global__ __launch_bounds__(kThreads) void topk_resolve_kernel(TopkArgs a) {
     if (l == 63) sh.wave_tot[w] = incl;
     __syncthreads();
     const int wt = l < kWaves ? sh.wave_tot[l] : 0;
-    const int wincl = wave_incl_sum(wt);
+    const int wincl = row16_scan_dpp(wt, 0, OpAdd());  // lanes 0..15: the waves' running totals
     int p = sh.split_before + sh.kept_before + readlane(wincl - wt, w) + incl - mine;
     while (sel) {
         const int b = __builtin_ctz(sel);
@@ -1808,7 +1808,7 @@ __device__ __forceinline__ bool select_from_lists(Shared &sh, const TopkArgs &a,
     if (l == 63) sh.wave_tot[w] = incl;
     __syncthreads();
     const int wt = l < kWaves ? sh.wave_tot[l] : 0;
-    const int wincl = wave_incl_sum(wt);
+    const int wincl = row16_scan_dpp(wt, 0, OpAdd());  // lanes 0..15: the waves' running totals
     int p = readlane(wincl - wt, w) + incl - mine;
     for (int u = 0; u < per; ++u) {
         if (w0 + u >= nw) break;
