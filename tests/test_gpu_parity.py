@@ -638,6 +638,26 @@ def test_topk_rows_map_from_previous_row():
     assert_topk_exact(g, oracle.topk(x, ctx, k), label="map from previous row")
 
 
+def test_topk_rows_at_the_register_width():
+    """One workgroup per row at the widest rows the register path holds (32,768
+    columns: every float4 group of every thread live, the kept set's 128
+    slices all full) and just past it (set aside), with rows just above k and
+    a ragged last group, several rows per workgroup: every row equals the
+    oracle."""
+    W, k, R = 32768 + 16, 2048, 300
+    rng = np.random.default_rng(3232)
+    choices = np.array([32768, 32767, 32766, 32765, 32769, 32784, k + 1, k + 3, 4097, 30001])
+    ctx = choices[rng.integers(0, len(choices), size=R)]
+    kinds = ["normal", "relu", "normal", "offset"]
+    x = np.concatenate([qsa_inputs.make_logits(1, W, [int(ctx[r])], seed=7000 + r, kind=kinds[r % 4])
+                        for r in range(R)])
+    say("topk rows at the register width")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    g = gpu_topk(xt, ct, k, workspace=None).cpu().numpy()
+    assert_topk_exact(g, oracle.topk(x, ctx, k), label="register width")
+
+
 def test_topk_sample_miss_falls_back():
     """Rows whose sampled columns are far below (or above) the rest: the
     sample's window misses the k-th value and the row takes the histogram
