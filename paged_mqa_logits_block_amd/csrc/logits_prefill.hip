@@ -22,10 +22,9 @@ namespace {
 // barriers the consumer waves drift apart, so that one wave's LDS reads and
 // stores overlap another's MFMAs instead of every wave waiting on the same
 // pipe at once (one barrier per step was 11% slower, one per 4 steps 1.5%).
-// The consumers issue no global loads
-// in the loop, so their stores never wait behind a key fetch (loads and
-// stores share one counter on gfx9).  Steps past the workgroup's visible
-// range only store -inf.
+// The consumers issue no global loads in the loop, so their stores never wait
+// behind a key fetch (loads and stores share one counter on gfx9).  Steps past
+// the workgroup's visible range only store -inf.
 //
 // Each consumer holds its 16 rows as 64 stacked (row, head) pairs in two
 // 32-row M tiles with Q resident.  The 32x32 accumulator gives lane l the 4
