@@ -54,9 +54,12 @@ KERNEL_FILES = {"paged_logits_kernel": "logits_decode.hip", "looped_logits_kerne
 COMMON_SOURCES = ("logits.hip", "logits_frag.h", "qsa_device.h", "qsa_internal.h")
 TOPK_COMMON_SOURCES = ("qsa_device.h", "qsa_internal.h")
 # the top-k launch rule of the library's planner: rows shared by several
-# workgroups for at most 128 rows wider than 4096 columns (with a workspace)
+# workgroups (with a workspace) for at most 128 rows wider than 4096 columns,
+# unless 48 or more rows fit the register path (32,768 columns)
 TOPK_SPLIT_MAX_ROWS = 128
 TOPK_SPLIT_MIN_WIDTH = 4097
+TOPK_ROWS_MIN_ROWS = 48
+TOPK_REGISTER_WIDTH = 32768
 
 DESCRIPTIONS = {
     "tiny": "2 requests x 4 rows, 4 heads, D=128, bf16, ctx 1000/3000, block 16, top-k 256",
@@ -331,7 +334,8 @@ def write_mfma(workload, kernel, folder):
 def topk_plan(inp):
     """Which top-k kernels the library runs for this shape with its automatic
     workspace: "split" (window + resolve kernels) or "rows" (one kernel)."""
-    if inp.num_rows <= TOPK_SPLIT_MAX_ROWS and inp.width >= TOPK_SPLIT_MIN_WIDTH:
+    r, w = inp.num_rows, inp.width
+    if r <= TOPK_SPLIT_MAX_ROWS and w >= TOPK_SPLIT_MIN_WIDTH and not (r >= TOPK_ROWS_MIN_ROWS and w <= TOPK_REGISTER_WIDTH):
         return "split"
     return "rows"
 

@@ -189,9 +189,10 @@ QSA_API qsa_status qsa_paged_logits_check(const void *q, const float *w, const v
  *              row is selected by one workgroup.  Otherwise it must hold at
  *              least qsa_topk_workspace_bytes(num_rows, width, k) bytes (else
  *              QSA_E_INVALID) at a 16-byte aligned address (else QSA_E_ALIGN).
- *              When that size is non-zero (at most 128 rows, width > 4096), each
- *              row is shared by several workgroups in two kernels that pass
- *              counts and candidates through the workspace.  Its contents need
+ *              When that size is non-zero (at most 128 rows, width > 4096,
+ *              and fewer than 48 rows or width > 32768), each row is shared
+ *              by several workgroups in two kernels that pass counts and
+ *              candidates through the workspace.  Its contents need
  *              no initialisation and are not kept between calls; calls that
  *              share a workspace must be ordered (same stream).  The selection
  *              does not depend on which path runs.

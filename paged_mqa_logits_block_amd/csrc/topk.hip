@@ -72,7 +72,6 @@ struct Shared {
     int ncand;
     int tie_col;
     uint32_t thr_key;
-    int ties_cut;  // some keys equal to the k-th are dropped (the column order decides)
     int ntie;      // fused selection: the tie group's count
     // register path: the previous row's kept columns (n <= kStage < 65536),
     // written out after the next row's first barrier, and the kept counts of
@@ -652,8 +651,8 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
 // ---- register-resident selection of a finite row ---------------------------
 //
 // The same selection as select_staged for the common case -- every visible
-// value finite, at most kCand values in the crossing bucket, and every value
-// equal to the k-th one kept (no tie that the column order has to break) --
+// value finite, at most kCand values in the crossing bucket, and, when the
+// column order has to break a tie at the k-th value, at most 64 of them --
 // with the row kept in registers and compared as floats, so that each pass
 // costs a few vector operations per element:
 //  * range: NaN-propagating max3/min3 (a NaN or an infinity sends the row to
@@ -665,8 +664,10 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
 //    everything below 1 and the last everything from kBins-3 up, so the
 //    crossing bucket's members are found by two compares on f;
 //  * the kept set: v >= T as floats (for finite values the float order with
-//    +0 == -0 is the key order), which needs every key equal to T kept.
-// A row where the column order has to drop some keys equal to T is set aside.
+//    +0 == -0 is the key order) when every key equal to T is kept; when the
+//    column order drops some, v > T or (v == T and column <= Ct), with Ct the
+//    k-th pair's column (found by the one-wave ranking of a short member
+//    list; a row with a longer list and such a tie is set aside).
 // The kept columns are ranked in column order into LDS and written with
 // contiguous stores.  Returns false, having written nothing, in any other case.
 
@@ -843,6 +844,10 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     // waves ranking it each for itself, without the barrier, were slower once
     // the kept set needed fewer barriers)
     uint32_t T;
+    // a tie at T that the column order cuts: the values equal to T are kept
+    // at columns <= Ct only, else Ct = INT_MAX (a short member list settles
+    // it here; a long one leaves the path)
+    int Ct = 0x7FFFFFFF;
     if (nc <= 64) {
         if (w == 0) {
             const uint32_t mk = l < nc ? sh.cand_key[l] : 0u;
@@ -860,14 +865,11 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
             const uint32_t tk = (uint32_t)readlane((int)mk, kl);
             const int tc = readlane(mc, kl);
             const bool cut = ballot(l < nc && mk == tk && mc > tc) != 0ull;
-            if (l == 0) sh.ties_cut = cut;
+            if (l == 0) sh.tie_col = cut ? tc : 0x7FFFFFFF;
         }
         __syncthreads();
         T = sh.thr_key;
-        if (sh.ties_cut) {
-            __syncthreads();
-            return false;
-        }
+        Ct = __builtin_amdgcn_readfirstlane(sh.tie_col);
     } else {
         radix_select(sh, [&](auto f) {
             for (int j = t; j < nc; j += kThreads) f(sh.cand_key[j]);
@@ -891,12 +893,29 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     // slices.  Each wave then clears its part of the histogram for the next row.
     uint8_t *wf = reinterpret_cast<uint8_t *>(sh.hist) + 512 * w;
     static_assert(kStageGroups * kThreads <= (int)sizeof(uint32_t) * kBins, "a byte per group fits the histogram");
+    if (Ct == 0x7FFFFFFF) {
 #pragma unroll
-    for (int j = 0; j < kStageGroups; ++j) {
-        uint32_t nib = 0u;
+        for (int j = 0; j < kStageGroups; ++j) {
+            uint32_t nib = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nib |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << e;
-        wf[64 * j + l] = (uint8_t)nib;
+            for (int e = 0; e < 4; ++e) nib |= (((x[j][e] >= Tf) & (4 * (t + kThreads * j) + e < n)) ? 1u : 0u) << e;
+            wf[64 * j + l] = (uint8_t)nib;
+        }
+    } else {  // (Ct < n)
+        // column tests of their own: shared with the branch above, the
+        // compiler hoists them out of both into scalar masks that spill
+        int tc = t;
+        asm volatile("" : "+v"(tc));
+#pragma unroll
+        for (int j = 0; j < kStageGroups; ++j) {
+            uint32_t nib = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int col = 4 * (tc + kThreads * j) + e;
+                nib |= (((x[j][e] > Tf) & (col < n)) | ((x[j][e] == Tf) & (col <= Ct)) ? 1u : 0u) << e;
+            }
+            wf[64 * j + l] = (uint8_t)nib;
+        }
     }
     const uint2 fw = reinterpret_cast<const uint2 *>(wf)[l];  // lanes 8 (l % 8) .. +7 of slice l / 8
     {
@@ -1128,6 +1147,10 @@ constexpr int kSlotLoads = 8;         // member slots a resolve thread loads
 constexpr int kHistLoads = 5;         // histogram words a resolve thread loads (17 slices)
 constexpr int kSplitCUs = 256;        // workgroups that fill the chip once
 constexpr int kSplitMaxRows = kSplitCUs / 2;
+// From this many rows, rows that fit the register path (width <= kStage) take
+// one workgroup each: 64 rows of 32,768 columns in 13.4 us against 14.3 us
+// split; 36 rows of 29,408 columns 13.2 against 13.4 us
+constexpr int kRowsMinRows = 48;
 constexpr int kRowsGrid = 256;         // one workgroup per CU (LDS)
 
 struct WindowShared {
@@ -1857,6 +1880,7 @@ int topk_groups_for_width(int width) { return width <= kMaxWidth ? 1 : 0; }
 TopkPlan plan_topk(int num_rows, int width) {
     TopkPlan p{1, width, 0, 0};
     if (num_rows <= 0 || num_rows > kSplitMaxRows || width <= 4 * kThreads) return p;
+    if (num_rows >= kRowsMinRows && width <= kStage) return p;
     const int by_len = (width + 4 * kThreads - 1) / (4 * kThreads);  // slices of >= 4096 columns
     const int min_sl = (width + 4 * kThreads * kSliceGroups - 1) / (4 * kThreads * kSliceGroups);
     int sl = kSplitCUs / num_rows;  // one round of workgroups

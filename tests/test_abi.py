@@ -149,12 +149,14 @@ def test_topk_validation(args, status):
 
 
 @pytest.mark.parametrize("rows,width,split", [
-    (36, 29408, True), (64, 65600, True), (64, 32768, True), (128, 8192, True), (15, 69632, True),
-    (8, 3008, False), (36, 4096, False), (129, 29408, False), (16384, 28672, False), (0, 29408, False),
+    (36, 29408, True), (64, 65600, True), (47, 32768, True), (48, 32769, True), (128, 32772, True),
+    (15, 69632, True), (8, 3008, False), (36, 4096, False), (48, 32768, False), (64, 32768, False),
+    (128, 8192, False), (129, 29408, False), (16384, 28672, False), (0, 29408, False),
 ])
 def test_topk_workspace_size(rows, width, split):
-    """Few long rows use the split selection (a workspace); many rows, or rows
-    of at most 4096 columns, use one workgroup per row (no workspace)."""
+    """Up to 47 rows of more than 4096 columns, or up to 128 rows wider than
+    the register path's 32,768 columns, use the split selection (a workspace);
+    other shapes use one workgroup per row (no workspace)."""
     nbytes = m.topk_workspace_bytes(rows, width, 2048)
     assert (nbytes > 0) == split, nbytes
     if split:  # counts, a 256-bucket histogram and <= 8192 member slots of 8 bytes per row
@@ -198,3 +200,26 @@ def test_topk_row_starts_need_no_host_check():
     base = (A, 3008, A, 8, 3008, 256, A, None, 0)
     assert m.topk_check(*base) == m.OK
     assert m.topk_check(*base, row_starts_ptr=A) == m.OK
+
+
+def test_bench_topk_plan_matches_the_library():
+    """bench.py names the top-k kernels it times from its own copy of the
+    planner's rule; it agrees with the library's workspace query on every
+    workload and at the rule's edges."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    class Shape:
+        def __init__(self, num_rows, width):
+            self.num_rows, self.width = num_rows, width
+
+    # the edges, and the workloads' (rows, width): tiny, decode_verify (and its
+    # fp16 and D = 64 forms), single_row_mixed, the fp8 4-row shapes, ragged
+    # and prefill_chunk
+    shapes = [Shape(r, w) for r in (1, 36, 47, 48, 64, 128, 129) for w in (4096, 4097, 32768, 32769, 65600)]
+    shapes += [Shape(r, w) for r, w in ((8, 3008), (36, 29408), (64, 65600), (64, 32768), (63, 32768),
+                                        (16384, 28672))]
+    for s in shapes:
+        split = m.topk_workspace_bytes(s.num_rows, s.width, 2048) > 0
+        assert (bench.topk_plan(s) == "split") == split, (s.num_rows, s.width)

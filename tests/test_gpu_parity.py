@@ -658,6 +658,48 @@ def test_topk_rows_at_the_register_width():
     assert_topk_exact(g, oracle.topk(x, ctx, k), label="register width")
 
 
+def _tied_at_kth(x, n, k, rng, below, above, zero=False):
+    """Row x (visible [0, n)): copies of its k-th largest value planted at
+    `below` random columns from under it and `above` from over it, so that the
+    column order has to cut a tie at the k-th value (the lowest columns of the
+    tie group are kept).  zero: the row is first shifted so that the k-th value
+    is 0.0, and the copies alternate between +0.0 and -0.0."""
+    v = x[:n]
+    order = np.argsort(-v, kind="stable")
+    if zero:
+        v -= v[order[k - 1]]
+    t = v[order[k - 1]]
+    cols = np.concatenate([rng.choice(order[k:], size=below, replace=False),
+                           rng.choice(order[:k - 1], size=above, replace=False)])
+    v[cols] = t
+    if zero:
+        v[cols[::2]] = np.float32(-0.0)
+    return x
+
+
+def test_topk_rows_tie_at_kth_cut_by_column():
+    """Rows whose k-th value is repeated past the cut, on the register path (one
+    workgroup per row, 2-3 rows per workgroup, each row's histogram on the
+    previous row's map): 1..40 copies of it planted under it and 0..20 over it,
+    some at columns before the k-th one's; ties of +0.0 and -0.0 at a k-th value
+    of 0; each row equals the oracle (equal values kept in column order)."""
+    W, k, R = 28672, 2048, 600
+    rng = np.random.default_rng(4242)
+    ctx = rng.integers(k + 64, W + 1, size=R)
+    x = (rng.standard_normal((R, W)).astype(np.float32) * np.float32(10.0))
+    for r in range(R):
+        n = int(ctx[r])
+        x[r, n:] = -np.inf
+        below = int(rng.choice([1, 2, 3, 8, 20, 40]))
+        above = int(rng.choice([0, 0, 1, 5, 20]))
+        _tied_at_kth(x[r], n, k, rng, below, above, zero=(r % 10 == 9))
+    say("topk rows tie at k-th cut by column")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    g = gpu_topk(xt, ct, k, workspace=None).cpu().numpy()
+    assert_topk_exact(g, oracle.topk(x, ctx, k), label="tie at k-th")
+
+
 def test_topk_sample_miss_falls_back():
     """Rows whose sampled columns are far below (or above) the rest: the
     sample's window misses the k-th value and the row takes the histogram
