@@ -651,9 +651,8 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
 // ---- register-resident selection of a finite row ---------------------------
 //
 // The same selection as select_staged for the common case -- every visible
-// value finite, at most kCand values in the crossing bucket, and, when the
-// column order has to break a tie at the k-th value, at most 64 of them --
-// with the row kept in registers and compared as floats, so that each pass
+// value finite and at most kCand values in the crossing bucket -- with the
+// row kept in registers and compared as floats, so that each pass
 // costs a few vector operations per element:
 //  * range: NaN-propagating max3/min3 (a NaN or an infinity sends the row to
 //    select_staged);
@@ -666,8 +665,8 @@ __device__ __forceinline__ void select_full_row(Shared &sh, const float *src, in
 //  * the kept set: v >= T as floats (for finite values the float order with
 //    +0 == -0 is the key order) when every key equal to T is kept; when the
 //    column order drops some, v > T or (v == T and column <= Ct), with Ct the
-//    k-th pair's column (found by the one-wave ranking of a short member
-//    list; a row with a longer list and such a tie is set aside).
+//    k-th pair's column (from the one-wave ranking of a short member list, or
+//    a radix select over the tied members' columns).
 // The kept columns are ranked in column order into LDS and written with
 // contiguous stores.  Returns false, having written nothing, in any other case.
 
@@ -845,8 +844,7 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
     // the kept set needed fewer barriers)
     uint32_t T;
     // a tie at T that the column order cuts: the values equal to T are kept
-    // at columns <= Ct only, else Ct = INT_MAX (a short member list settles
-    // it here; a long one leaves the path)
+    // at columns <= Ct only, else Ct = INT_MAX
     int Ct = 0x7FFFFFFF;
     if (nc <= 64) {
         if (w == 0) {
@@ -874,9 +872,17 @@ __device__ __forceinline__ bool select_fast(Shared &sh, f32x4 (&x)[kStageGroups]
         radix_select(sh, [&](auto f) {
             for (int j = t; j < nc; j += kThreads) f(sh.cand_key[j]);
         }, T, need, cnt);
-        if (cnt > need) {  // the column order decides among equal values
-            __syncthreads();
-            return false;
+        if (cnt > need) {
+            // the column order decides among the cnt members equal to T: Ct is
+            // the need-th smallest of their columns (columns < 65536, so the
+            // need-th largest of 0xFFFF - column; columns are distinct)
+            uint32_t cm;
+            int need2 = need, cnt2 = 0;
+            radix_select(sh, [&](auto f) {
+                for (int j = t; j < nc; j += kThreads)
+                    if (sh.cand_key[j] == T) f(0xFFFFu - (uint32_t)sh.cand_col[j]);
+            }, cm, need2, cnt2);
+            Ct = __builtin_amdgcn_readfirstlane(0xFFFF - (int)cm);
         }
     }
     const float Tf = key_value(T);

@@ -680,9 +680,11 @@ def _tied_at_kth(x, n, k, rng, below, above, zero=False):
 def test_topk_rows_tie_at_kth_cut_by_column():
     """Rows whose k-th value is repeated past the cut, on the register path (one
     workgroup per row, 2-3 rows per workgroup, each row's histogram on the
-    previous row's map): 1..40 copies of it planted under it and 0..20 over it,
-    some at columns before the k-th one's; ties of +0.0 and -0.0 at a k-th value
-    of 0; each row equals the oracle (equal values kept in column order)."""
+    previous row's map): 1..300 copies of it planted under it and 0..20 over it,
+    some at columns before the k-th one's (more than 64 members in the crossing
+    bucket take the radix select, fewer the one-wave ranking); ties of +0.0 and
+    -0.0 at a k-th value of 0; each row equals the oracle (equal values kept in
+    column order)."""
     W, k, R = 28672, 2048, 600
     rng = np.random.default_rng(4242)
     ctx = rng.integers(k + 64, W + 1, size=R)
@@ -690,7 +692,7 @@ def test_topk_rows_tie_at_kth_cut_by_column():
     for r in range(R):
         n = int(ctx[r])
         x[r, n:] = -np.inf
-        below = int(rng.choice([1, 2, 3, 8, 20, 40]))
+        below = int(rng.choice([1, 2, 3, 8, 20, 40, 100, 300]))
         above = int(rng.choice([0, 0, 1, 5, 20]))
         _tied_at_kth(x[r], n, k, rng, below, above, zero=(r % 10 == 9))
     say("topk rows tie at k-th cut by column")
