@@ -677,6 +677,32 @@ def _tied_at_kth(x, n, k, rng, below, above, zero=False):
     return x
 
 
+@pytest.mark.parametrize("rows,W", [(47, 32768), (48, 32768), (48, 32772), (128, 32768), (128, 32772)])
+def test_topk_planner_row_rule_edges(rows, W):
+    """Either side of the planner's rule (47 rows split, 48 rows of at most
+    32,768 columns one workgroup per row, wider rows split again), with the
+    automatic workspace, ragged counts, some rows at the full width and a tie
+    at the k-th value past the cut in every third row: the workspace query says
+    which path runs, and every row equals the oracle."""
+    m = qsa()
+    k = 2048
+    rng = np.random.default_rng(rows * 100003 + W)
+    ctx = rng.integers(k + 1, W + 1, size=rows)
+    ctx[:3] = [W, W - 1, k + 1]
+    x = (rng.standard_normal((rows, W)).astype(np.float32) * np.float32(10.0))
+    for r in range(rows):
+        x[r, int(ctx[r]):] = -np.inf
+        if r % 3 == 0:
+            _tied_at_kth(x[r], int(ctx[r]), k, rng, int(rng.integers(1, 50)), int(rng.integers(0, 5)))
+    split = m.topk_workspace_bytes(rows, W, k) > 0
+    assert split == (rows < 48 or W > 32768)
+    say("topk planner edge", rows, W, "split" if split else "rows")
+    xt = torch.from_numpy(x).cuda()
+    ct = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    g = gpu_topk(xt, ct, k).cpu().numpy()
+    assert_topk_exact(g, oracle.topk(x, ctx, k), label=f"planner edge {rows}x{W}")
+
+
 def test_topk_rows_tie_at_kth_cut_by_column():
     """Rows whose k-th value is repeated past the cut, on the register path (one
     workgroup per row, 2-3 rows per workgroup, each row's histogram on the
